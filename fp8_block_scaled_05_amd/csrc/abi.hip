@@ -1,0 +1,171 @@
+// C ABI of libfp8bs: argument validation (before any HIP call) and dispatch
+// to the gfx950 kernels.  Declarations and the contract are in
+// include/fp8bs.h.
+
+#include "fp8bs.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kTile = 128;
+constexpr int64_t kMaxGroups = 4096;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool ld_ok(int64_t ld, int64_t row) { return ld >= row && ld % 16 == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FP8BS_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return FP8BS_ERR_HIP;
+}
+
+size_t fused_q_bytes(int64_t M, int64_t K) { return round256(size_t(M) * size_t(K)); }
+size_t fused_s_bytes(int64_t M, int64_t K) { return round256(size_t(K / kTile) * size_t(M) * 4); }
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                        int64_t ldq, float* s, int64_t lds, void* stream) {
+  if (M < 0 || K <= 0 || K % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0) return FP8BS_OK;
+  if (!x || !q || !s) return FP8BS_ERR_NULL;
+  if (!ld_ok(ldx, K) || !ld_ok(ldq, K) || lds < M) return FP8BS_ERR_LAYOUT;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8BS_ERR_LAYOUT;
+  return hip_status(fp8bs::launch_quant_act(x, M, K, ldx, q, ldq, s, lds,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                        int64_t ldq, float* s, void* stream) {
+  if (N < 0 || K <= 0 || K % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (N == 0) return FP8BS_OK;
+  if (!w || !q || !s) return FP8BS_ERR_NULL;
+  if (!ld_ok(ldw, K) || !ld_ok(ldq, K)) return FP8BS_ERR_LAYOUT;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8BS_ERR_LAYOUT;
+  return hip_status(
+      fp8bs::launch_quant_w(w, N, K, ldw, q, ldq, s, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa, int64_t ldsa,
+                   const uint8_t* b, int64_t ldb, const float* sb, void* c, int64_t ldc,
+                   int out_kind, int64_t M, int64_t N, int64_t K, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (a_kind != FP8BS_A_E4M3 && a_kind != FP8BS_A_BF16) return FP8BS_ERR_DTYPE;
+  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || K % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!a || !b || !sb || !c) return FP8BS_ERR_NULL;
+  if (a_kind == FP8BS_A_E4M3 && !sa) return FP8BS_ERR_NULL;
+  if (!ld_ok(lda, K) || !ld_ok(ldb, K) || ldc < N) return FP8BS_ERR_LAYOUT;
+  if (sa && ldsa < M) return FP8BS_ERR_LAYOUT;
+  const uintptr_t c_align = out_kind == FP8BS_OUT_F32 ? 4 : 2;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sb, 4) ||
+      (sa && !aligned(sa, 4)))
+    return FP8BS_ERR_LAYOUT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  fp8bs::GemmArgs g{};
+  g.b = b;
+  g.ldb = ldb;
+  g.sb = sb;
+  g.c = c;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  if (a_kind == FP8BS_A_E4M3) {
+    g.a = static_cast<const uint8_t*>(a);
+    g.lda = lda;
+    g.sa = sa;
+    g.ldsa = ldsa;
+  } else {
+    const size_t need = fp8bs_workspace_bytes(FP8BS_OP_GEMM_BF16, M, N, K, 0);
+    if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return FP8BS_ERR_LAYOUT;
+    uint8_t* wq = static_cast<uint8_t*>(workspace);
+    float* ws = sa ? sa : reinterpret_cast<float*>(wq + fused_q_bytes(M, K));
+    const int64_t wlds = sa ? ldsa : M;
+    int st0 = hip_status(fp8bs::launch_quant_act(static_cast<const uint16_t*>(a), M, K, lda, wq,
+                                                 K, ws, wlds, st));
+    if (st0 != FP8BS_OK) return st0;
+    g.a = wq;
+    g.lda = K;
+    g.sa = ws;
+    g.ldsa = wlds;
+  }
+  return hip_status(fp8bs::launch_block_gemm(g, out_kind == FP8BS_OUT_BF16, st));
+}
+
+int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                           const uint8_t* b, int64_t ldb, int64_t b_group_stride,
+                           const float* sb, void* c, int64_t ldc, int out_kind,
+                           const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N,
+                           int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+  if (G < 1 || G > kMaxGroups || M_total < 0 || N < 0 || K <= 0 || K % kTile != 0)
+    return FP8BS_ERR_SHAPE;
+  if (M_total == 0 || N == 0) return FP8BS_OK;
+  if (!a || !sa || !b || !sb || !c || !group_offsets) return FP8BS_ERR_NULL;
+  if (!ld_ok(lda, K) || !ld_ok(ldb, K) || ldc < N || ldsa < M_total) return FP8BS_ERR_LAYOUT;
+  if (b_group_stride % 16 != 0 || b_group_stride < (N - 1) * ldb + K) return FP8BS_ERR_LAYOUT;
+  const uintptr_t c_align = out_kind == FP8BS_OUT_F32 ? 4 : 2;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sa, 4) ||
+      !aligned(sb, 4) || !aligned(group_offsets, 4))
+    return FP8BS_ERR_LAYOUT;
+  fp8bs::GemmArgs g{};
+  g.a = a;
+  g.lda = lda;
+  g.sa = sa;
+  g.ldsa = ldsa;
+  g.b = b;
+  g.ldb = ldb;
+  g.b_group_stride = b_group_stride;
+  g.sb = sb;
+  g.c = c;
+  g.ldc = ldc;
+  g.M = M_total;
+  g.N = N;
+  g.K = K;
+  g.group_offsets = group_offsets;
+  g.G = G;
+  return hip_status(fp8bs::launch_grouped_gemm(g, out_kind == FP8BS_OUT_BF16,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t G) {
+  (void)N;
+  (void)G;
+  if (M <= 0 || K <= 0) return 0;
+  switch (op) {
+    case FP8BS_OP_GEMM_BF16:
+      return fused_q_bytes(M, K) + fused_s_bytes(M, K);
+    default:
+      return 0;
+  }
+}
+
+const char* fp8bs_status_string(int status) {
+  switch (status) {
+    case FP8BS_OK: return "ok";
+    case FP8BS_ERR_NULL: return "a required pointer is NULL";
+    case FP8BS_ERR_SHAPE: return "unsupported shape (negative size, K not a positive multiple of 128, or bad group count)";
+    case FP8BS_ERR_LAYOUT: return "unsupported layout (leading dimension or pointer alignment)";
+    case FP8BS_ERR_DTYPE: return "unknown a_kind or out_kind";
+    case FP8BS_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8BS_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fp8bs_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Launchers behind the C ABI (arguments already validated by abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+struct GemmArgs {
+  const uint8_t* a;
+  int64_t lda;
+  const float* sa;
+  int64_t ldsa;
+  const uint8_t* b;
+  int64_t ldb;
+  int64_t b_group_stride;  // bytes between experts' weights (grouped only)
+  const float* sb;
+  void* c;
+  int64_t ldc;
+  int64_t M;  // rows (dense) or M_total (grouped)
+  int64_t N;
+  int64_t K;
+  const int32_t* group_offsets;  // grouped only, device, G+1 entries
+  int64_t G;
+};
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                            hipStream_t stream);
+
+hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                          uint8_t* q, int64_t ldq, float* s, hipStream_t stream);
+
+hipError_t launch_block_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream);
+
+}  // namespace fp8bs

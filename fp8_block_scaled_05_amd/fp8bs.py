@@ -1,0 +1,197 @@
+"""Thin Python binding of libfp8bs (C ABI in include/fp8bs.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory (tensors) and the current stream.
+Importing this module loads ``libfp8bs.so`` from the package directory and
+raises ``ImportError`` if it has not been built (there is no fallback).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8bs.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_LAYOUT, ERR_DTYPE, ERR_WORKSPACE, ERR_HIP = range(7)
+OUT_F32, OUT_BF16 = 0, 1
+A_E4M3, A_BF16 = 0, 1
+OP_QUANT_ACT, OP_QUANT_W, OP_GEMM_E4M3, OP_GEMM_BF16, OP_GROUPED_GEMM = range(5)
+
+EXPORTS = (
+    "fp8_quant_act_1x128",
+    "fp8_quant_w_128x128",
+    "fp8_block_gemm",
+    "fp8_block_grouped_gemm",
+    "fp8bs_workspace_bytes",
+    "fp8bs_status_string",
+    "fp8bs_last_hip_error",
+)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "fp8_quant_act_1x128": ([_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _int),
+    "fp8_quant_w_128x128": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p], _int),
+    "fp8_block_gemm": ([_int, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _int,
+                        _i64, _i64, _i64, _p, _sz, _p], _int),
+    "fp8_block_grouped_gemm": ([_p, _i64, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _int,
+                                _p, _i64, _i64, _i64, _i64, _p, _sz, _p], _int),
+    "fp8bs_workspace_bytes": ([_int, _i64, _i64, _i64, _i64], _sz),
+    "fp8bs_status_string": ([_int], ctypes.c_char_p),
+    "fp8bs_last_hip_error": ([], _int),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m fp8_block_scaled_05_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+class Fp8bsError(RuntimeError):
+    def __init__(self, status, where):
+        msg = lib.fp8bs_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError_t {lib.fp8bs_last_hip_error()})"
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(status, where):
+    if status != OK:
+        raise Fp8bsError(status, where)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libfp8bs works on GPU tensors only")
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def _ld(t):
+    # leading dimension of a row-major 2-D tensor (its row stride)
+    return t.stride(0) if t.dim() == 2 else t.shape[-1]
+
+
+def workspace_bytes(op, M, N, K, G=0):
+    return int(lib.fp8bs_workspace_bytes(op, M, N, K, G))
+
+
+def fp8_quant_act_1x128(x, q=None, s=None, lds=None):
+    """bf16 [M][K] -> (E4M3 codes uint8 [M][K], scales fp32 [K/128][lds]).
+
+    ``s[kb, m]`` is the scale of row m's tile kb (``lds >= M``, default M).
+    """
+    _need_device(x, q, s)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    M, K = x.shape
+    ldx = _rowmajor(x, "x") if M else K
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(K // 128, lds or M, dtype=torch.float32, device=x.device)
+    lds = s.shape[1] if s.dim() == 2 else (lds or M)
+    _check(lib.fp8_quant_act_1x128(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), lds,
+                                   _stream(x)), "fp8_quant_act_1x128")
+    return q, s
+
+
+def fp8_quant_w_128x128(w, q=None, s=None):
+    """bf16 [N][K] -> (E4M3 codes uint8 [N][K], scales fp32 [ceil(N/128)][K/128])."""
+    _need_device(w, q, s)
+    if w.dtype != torch.bfloat16:
+        raise ValueError("w must be bfloat16")
+    N, K = w.shape
+    ldw = _rowmajor(w, "w") if N else K
+    if q is None:
+        q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty((N + 127) // 128, K // 128, dtype=torch.float32, device=w.device)
+    _check(lib.fp8_quant_w_128x128(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _stream(w)),
+           "fp8_quant_w_128x128")
+    return q, s
+
+
+def _out_kind(dtype):
+    if dtype == torch.bfloat16:
+        return OUT_BF16
+    if dtype == torch.float32:
+        return OUT_F32
+    raise ValueError("output must be float32 or bfloat16")
+
+
+def fp8_block_gemm(a, sa, b, sb, out=None, out_dtype=torch.bfloat16, workspace=None):
+    """C[M][N] = A . B^T with per-tile/per-block scales and FP32 promotion.
+
+    ``a`` uint8 E4M3 codes with input scales ``sa`` [K/128][ldsa], or
+    bfloat16 (quantized inside the call; ``sa`` is then an optional output of
+    the scales).  ``b`` uint8 [N][K], ``sb`` fp32 [ceil(N/128)][K/128].
+    """
+    _need_device(a, sa, b, sb, out, workspace)
+    a_kind = A_E4M3 if a.dtype == torch.uint8 else A_BF16 if a.dtype == torch.bfloat16 else None
+    if a_kind is None:
+        raise ValueError("a must be uint8 (E4M3 codes) or bfloat16")
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    ws_need = workspace_bytes(OP_GEMM_BF16, M, N, K) if a_kind == A_BF16 else 0
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ldsa = sa.shape[1] if sa is not None else 0
+    _check(lib.fp8_block_gemm(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
+                              _ptr(sb), _ptr(out), _ld(out), _out_kind(out.dtype), M, N, K,
+                              _ptr(workspace), ws_bytes, _stream(a)), "fp8_block_gemm")
+    return out
+
+
+def fp8_block_grouped_gemm(a, sa, b, sb, group_offsets, out=None, out_dtype=torch.bfloat16):
+    """Grouped (MoE) block GEMM.
+
+    ``a`` uint8 [M_total][K] rows sorted by expert, ``sa`` fp32 [K/128][ldsa];
+    ``b`` uint8 [G][N][K]; ``sb`` fp32 [G][ceil(N/128)][K/128];
+    ``group_offsets`` int32 [G+1] on the device.
+    """
+    _need_device(a, sa, b, sb, group_offsets, out)
+    if group_offsets.dtype != torch.int32:
+        raise ValueError("group_offsets must be int32")
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    if out is None:
+        out = torch.empty(M_total, N, dtype=out_dtype, device=a.device)
+    _check(lib.fp8_block_grouped_gemm(_ptr(a), _ld(a), _ptr(sa), sa.shape[1], _ptr(b),
+                                      b.stride(1), b.stride(0), _ptr(sb), _ptr(out), _ld(out),
+                                      _out_kind(out.dtype), _ptr(group_offsets), G, M_total, N,
+                                      K, None, 0, _stream(a)), "fp8_block_grouped_gemm")
+    return out

@@ -1,0 +1,184 @@
+/*
+ * fp8bs.h -- C ABI of the block-scaled FP8 library for AMD MI355X (gfx950).
+ *
+ * The method (DeepSeek-V3 style FP8 training, as described in the codingmall
+ * knowledge-base pages "How online quantization in DeepSeek-V3 differs from
+ * delayed quantization", "How the unified E4M3 format adds to DeepSeek-V3's
+ * efficiency" and "Advantages of using FP8 for GEMM operations in
+ * DeepSeek-V3"):
+ *   - activations are quantized to E4M3 per 1x128 tile and weights per
+ *     128x128 block, each group with its own scale computed on the fly from
+ *     the group's current maximum magnitude (no history of maxima);
+ *   - the FP8 GEMM promotes its partial sums to FP32 once per 128-wide K
+ *     group and applies the activation-tile and weight-block scales there.
+ *
+ * Numerics (identical on every entry point):
+ *   E4M3 is the OCP E4M3FN format (bias 7, max 448, no infinities).
+ *   For a group with largest magnitude amax:  a = max(amax, 2^-64),
+ *   s = RN32(a / 448) (stored scale), r = RN32(448 / a),
+ *   q = E4M3_RNE_saturating(RN32(x * r)).
+ *   GEMM:  C[m][n] = sum_kb S_A(m,kb) * S_W(n/128,kb) * P(m,n,kb), where
+ *   P is the FP8 x FP8 dot product over the 128 K values of group kb,
+ *   accumulated in FP32; the promotion is an FP32 multiply-add.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *     never allocates or frees device memory and keeps no state besides a
+ *     thread-local record of the last HIP error.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL means the default stream).  The return value is a
+ *     synchronous status: FP8BS_OK means "validated and enqueued"; a device
+ *     fault surfaces at the caller's next synchronisation.  On any other
+ *     status nothing has been enqueued.
+ *   - Matrices are row-major with K contiguous (A is [M][K], W/B is [N][K],
+ *     C is [M][N]); leading dimensions are in elements.
+ *   - K must be a positive multiple of 128.  M and N may be any value >= 0
+ *     (partial tiles at the edges are handled); a call with M == 0 or N == 0
+ *     returns FP8BS_OK and launches nothing.
+ *   - Leading dimensions must be >= the row length and multiples of 16;
+ *     tensor pointers must be 16-byte aligned.  Otherwise FP8BS_ERR_LAYOUT.
+ *   - Outputs must not alias inputs.  Calls are thread-safe.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  FP8BS_OK = 0,
+  FP8BS_ERR_NULL = 1,      /* a required pointer is NULL                     */
+  FP8BS_ERR_SHAPE = 2,     /* negative size, K not a multiple of 128, ...    */
+  FP8BS_ERR_LAYOUT = 3,    /* leading dimension or alignment not supported   */
+  FP8BS_ERR_DTYPE = 4,     /* unknown a_kind / out_kind                      */
+  FP8BS_ERR_WORKSPACE = 5, /* workspace missing or smaller than required     */
+  FP8BS_ERR_HIP = 6        /* a HIP launch failed (see fp8bs_last_hip_error) */
+};
+
+/* out_kind: element type of C. */
+enum { FP8BS_OUT_F32 = 0, FP8BS_OUT_BF16 = 1 };
+
+/* a_kind: element type of A in fp8_block_gemm. */
+enum { FP8BS_A_E4M3 = 0, FP8BS_A_BF16 = 1 };
+
+/* op ids for fp8bs_workspace_bytes. */
+enum {
+  FP8BS_OP_QUANT_ACT = 0,
+  FP8BS_OP_QUANT_W = 1,
+  FP8BS_OP_GEMM_E4M3 = 2,
+  FP8BS_OP_GEMM_BF16 = 3,
+  FP8BS_OP_GROUPED_GEMM = 4
+};
+
+/*
+ * Online activation quantization, one scale per 1x128 tile.
+ * Pages: "How online quantization in DeepSeek-V3 differs from delayed
+ * quantization", item 1 (scale per 1x128 activation tile, computed on the
+ * fly); "How the unified E4M3 format adds to DeepSeek-V3's efficiency",
+ * sections "Fine-grained quantization strategy" and "Dynamic scaling and
+ * online quantization".
+ *
+ *   x   [in]  bf16 bit patterns, [M][ldx]; columns 0..K-1 are read.
+ *   q   [out] E4M3 codes, [M][ldq].
+ *   s   [out] fp32 scales: s(m, kb) is stored at s[kb*lds + m], lds >= M,
+ *             for kb = 0..K/128-1 (layout M-contiguous per K group, the order
+ *             in which the GEMM reads them).
+ * Errors: NULL pointer -> ERR_NULL; M < 0, K <= 0, K % 128 -> ERR_SHAPE;
+ *         ldx/ldq < K or not multiples of 16, lds < M, misaligned pointer
+ *         -> ERR_LAYOUT.
+ */
+int fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                        uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                        void* stream);
+
+/*
+ * Online weight quantization, one scale per 128x128 block.
+ * Pages: "How online quantization in DeepSeek-V3 differs from delayed
+ * quantization", item 1 (scale per 128x128 weight block); "How the unified
+ * E4M3 format adds to DeepSeek-V3's efficiency", section "Fine-grained
+ * quantization strategy".
+ *
+ *   w   [in]  bf16 bit patterns, [N][ldw].
+ *   q   [out] E4M3 codes, [N][ldq].
+ *   s   [out] fp32 scales, row-major [ceil(N/128)][K/128]:
+ *             s(nb, kb) at s[nb*(K/128) + kb].  A partial last band (N not a
+ *             multiple of 128) takes its maximum over its valid rows.
+ * Errors: as fp8_quant_act_1x128.
+ */
+int fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                        uint8_t* q, int64_t ldq, float* s, void* stream);
+
+/*
+ * Block-scaled FP8 GEMM with FP32 promotion every 128 K:  C = A . B^T.
+ * Pages: "Advantages of using FP8 for GEMM operations in DeepSeek-V3",
+ * items 1, 5 and 8 (FP8 GEMM; partial sums promoted to FP32 registers at
+ * fixed intervals); "How the unified E4M3 format adds to DeepSeek-V3's
+ * efficiency", section "Enhanced numerical stability".
+ *
+ *   a_kind  FP8BS_A_E4M3: a is E4M3 codes [M][lda] and sa (input) holds the
+ *                         activation scales, sa(m,kb) at sa[kb*ldsa + m].
+ *           FP8BS_A_BF16: a is bf16 bit patterns [M][lda], quantized per
+ *                         1x128 tile inside the call exactly as
+ *                         fp8_quant_act_1x128 would; sa may be NULL, else the
+ *                         computed scales are written there (same layout).
+ *                         Needs a workspace of
+ *                         fp8bs_workspace_bytes(FP8BS_OP_GEMM_BF16, M, N, K, 0).
+ *   b, sb   E4M3 weight codes [N][ldb] and block scales
+ *           [ceil(N/128)][K/128] (layout of fp8_quant_w_128x128).
+ *   c       output [M][ldc], fp32 or bf16 (round-to-nearest-even) by out_kind.
+ * Errors: as above; unknown a_kind/out_kind -> ERR_DTYPE; workspace too
+ *         small -> ERR_WORKSPACE.
+ */
+int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa,
+                   int64_t ldsa, const uint8_t* b, int64_t ldb,
+                   const float* sb, void* c, int64_t ldc, int out_kind,
+                   int64_t M, int64_t N, int64_t K, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped (MoE) block-scaled FP8 GEMM: rows group_offsets[g] ..
+ * group_offsets[g+1]-1 of A are multiplied by expert g's weight.
+ * Pages: "Advantages of using FP8 for GEMM operations in DeepSeek-V3",
+ * item 8 (the FP8 GEMM serves dense and MoE layers).
+ *
+ *   a, sa         E4M3 codes [M_total][lda], scales sa(m,kb) at
+ *                 sa[kb*ldsa + m] (rows sorted by expert).
+ *   b             expert weights: expert g's [N][ldb] codes start at
+ *                 b + g*b_group_stride (bytes; multiple of 16).
+ *   sb            block scales sb(g,nb,kb) at
+ *                 sb[(g*ceil(N/128) + nb)*(K/128) + kb].
+ *   group_offsets DEVICE int32 [G+1], 0 = off[0] <= off[1] <= ... <=
+ *                 off[G] = M_total.  Read on the device (no host
+ *                 synchronisation); trusted, not validated.  Empty groups are
+ *                 allowed and write nothing.
+ * Errors: as above; G < 1 or G > 4096 -> ERR_SHAPE.
+ */
+int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa,
+                           int64_t ldsa, const uint8_t* b, int64_t ldb,
+                           int64_t b_group_stride, const float* sb, void* c,
+                           int64_t ldc, int out_kind,
+                           const int32_t* group_offsets, int64_t G,
+                           int64_t M_total, int64_t N, int64_t K,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Workspace bytes an entry point needs for the given sizes (0 if none). */
+size_t fp8bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
+                             int64_t G);
+
+/* Static description of a status code. */
+const char* fp8bs_status_string(int status);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int fp8bs_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol that include/fp8bs.h declares, and rejects bad arguments with the
+documented status before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+LIB = os.path.join(ROOT, "fp8_block_scaled_05_amd", "libfp8bs.so")
+
+
+@pytest.fixture(scope="module")
+def fp8bs():
+    if not os.path.exists(LIB):
+        # CPU-side convenience for a fresh checkout; GPU runs use the
+        # library built beforehand.
+        from fp8_block_scaled_05_amd import build
+        build.build()
+    from fp8_block_scaled_05_amd import fp8bs as mod
+    return mod
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for n in ("fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_block_gemm",
+              "fp8_block_grouped_gemm"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(fp8bs):
+    lib = ctypes.CDLL(LIB)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(fp8bs.EXPORTS)
+
+
+def test_status_strings(fp8bs):
+    lib = fp8bs.lib
+    for st in range(7):
+        assert lib.fp8bs_status_string(st)
+    assert lib.fp8bs_status_string(0) == b"ok"
+    assert b"unknown" in lib.fp8bs_status_string(99)
+    assert lib.fp8bs_last_hip_error() == 0
+
+
+# Fake, well-aligned device addresses: validation must reject the call before
+# touching them.
+P = 1 << 20
+
+
+def _qa(lib, x=P, M=64, K=256, ldx=256, q=P, ldq=256, s=P, lds=64):
+    return lib.fp8_quant_act_1x128(x, M, K, ldx, q, ldq, s, lds, None)
+
+
+def test_quant_act_validation(fp8bs):
+    lib = fp8bs.lib
+    assert _qa(lib, M=-1) == fp8bs.ERR_SHAPE
+    assert _qa(lib, K=0) == fp8bs.ERR_SHAPE
+    assert _qa(lib, K=200) == fp8bs.ERR_SHAPE
+    assert _qa(lib, M=0, x=0, q=0, s=0) == fp8bs.OK  # empty: nothing launched
+    assert _qa(lib, x=0) == fp8bs.ERR_NULL
+    assert _qa(lib, s=0) == fp8bs.ERR_NULL
+    assert _qa(lib, ldx=128) == fp8bs.ERR_LAYOUT
+    assert _qa(lib, ldx=264) == fp8bs.ERR_LAYOUT
+    assert _qa(lib, ldq=255) == fp8bs.ERR_LAYOUT
+    assert _qa(lib, lds=63) == fp8bs.ERR_LAYOUT
+    assert _qa(lib, x=P + 8) == fp8bs.ERR_LAYOUT
+    assert _qa(lib, s=P + 2) == fp8bs.ERR_LAYOUT
+
+
+def test_quant_w_validation(fp8bs):
+    lib = fp8bs.lib
+    f = lambda w=P, N=256, K=256, ldw=256, q=P, ldq=256, s=P: lib.fp8_quant_w_128x128(
+        w, N, K, ldw, q, ldq, s, None)
+    assert f(N=-3) == fp8bs.ERR_SHAPE
+    assert f(K=129) == fp8bs.ERR_SHAPE
+    assert f(N=0, w=0, q=0, s=0) == fp8bs.OK
+    assert f(q=0) == fp8bs.ERR_NULL
+    assert f(ldw=100) == fp8bs.ERR_LAYOUT
+    assert f(q=P + 4) == fp8bs.ERR_LAYOUT
+
+
+def _gemm(lib, a_kind=0, a=P, lda=256, sa=P, ldsa=64, b=P, ldb=256, sb=P, c=P, ldc=128,
+          out_kind=1, M=64, N=128, K=256, ws=0, ws_bytes=0):
+    return lib.fp8_block_gemm(a_kind, a, lda, sa, ldsa, b, ldb, sb, c, ldc, out_kind, M, N, K,
+                              ws, ws_bytes, None)
+
+
+def test_gemm_validation(fp8bs):
+    lib = fp8bs.lib
+    assert _gemm(lib, a_kind=7) == fp8bs.ERR_DTYPE
+    assert _gemm(lib, out_kind=5) == fp8bs.ERR_DTYPE
+    assert _gemm(lib, K=100) == fp8bs.ERR_SHAPE
+    assert _gemm(lib, N=-1) == fp8bs.ERR_SHAPE
+    assert _gemm(lib, M=0, a=0, b=0, c=0) == fp8bs.OK
+    assert _gemm(lib, N=0) == fp8bs.OK
+    assert _gemm(lib, sa=0) == fp8bs.ERR_NULL  # E4M3 A needs its scales
+    assert _gemm(lib, sb=0) == fp8bs.ERR_NULL
+    assert _gemm(lib, ldb=200) == fp8bs.ERR_LAYOUT
+    assert _gemm(lib, ldc=100) == fp8bs.ERR_LAYOUT
+    assert _gemm(lib, ldsa=10) == fp8bs.ERR_LAYOUT
+    assert _gemm(lib, c=P + 1) == fp8bs.ERR_LAYOUT
+    assert _gemm(lib, b=P + 8) == fp8bs.ERR_LAYOUT
+    # bf16 A needs a workspace of the advertised size
+    need = lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_BF16, 64, 128, 256, 0)
+    assert need >= 64 * 256 + 2 * 64 * 4
+    assert _gemm(lib, a_kind=1, sa=0) == fp8bs.ERR_WORKSPACE
+    assert _gemm(lib, a_kind=1, sa=0, ws=P, ws_bytes=need - 1) == fp8bs.ERR_WORKSPACE
+    assert _gemm(lib, a_kind=1, sa=0, ws=P + 16, ws_bytes=need) == fp8bs.ERR_LAYOUT
+
+
+def test_grouped_validation(fp8bs):
+    lib = fp8bs.lib
+
+    def g(a=P, lda=256, sa=P, ldsa=64, b=P, ldb=256, bstride=256 * 128, sb=P, c=P, ldc=128,
+          out_kind=1, off=P, G=4, M=64, N=128, K=256):
+        return lib.fp8_block_grouped_gemm(a, lda, sa, ldsa, b, ldb, bstride, sb, c, ldc,
+                                          out_kind, off, G, M, N, K, None, 0, None)
+
+    assert g(G=0) == fp8bs.ERR_SHAPE
+    assert g(G=5000) == fp8bs.ERR_SHAPE
+    assert g(K=64) == fp8bs.ERR_SHAPE
+    assert g(M=0) == fp8bs.OK
+    assert g(off=0) == fp8bs.ERR_NULL
+    assert g(bstride=256 * 127) == fp8bs.ERR_LAYOUT
+    assert g(bstride=256 * 128 + 8) == fp8bs.ERR_LAYOUT
+    assert g(ldsa=32) == fp8bs.ERR_LAYOUT
+    assert g(out_kind=3) == fp8bs.ERR_DTYPE
+
+
+def test_workspace_query(fp8bs):
+    lib = fp8bs.lib
+    assert lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_E4M3, 64, 128, 256, 0) == 0
+    assert lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_BF16, 0, 128, 256, 0) == 0
+    ws = lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_BF16, 64, 18432, 7168, 0)
+    assert ws % 256 == 0 and ws >= 64 * 7168 + 56 * 64 * 4
+
+
+def test_binding_refuses_cpu_tensors(fp8bs):
+    import torch
+    with pytest.raises(ValueError):
+        fp8bs.fp8_quant_act_1x128(torch.zeros(4, 128, dtype=torch.bfloat16))

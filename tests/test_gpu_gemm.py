@@ -1,0 +1,175 @@
+"""GPU parity of the dense block-scaled GEMM against the float64 oracle.
+
+The GEMM is fed codes and scales produced by the oracle's quantizer from the
+seeded bf16 inputs, so the oracle's operands never come from the GPU; every
+checked element must satisfy |C_gpu - C| <= 2e-3 * sum_k |a_k b_k|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_05_amd import synth
+from tests import _gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp8bs():
+    from fp8_block_scaled_05_amd import fp8bs as mod
+    return mod
+
+
+def _quantized(M, N, K, case, act_outlier=100.0, row_lognormal=True):
+    a = synth.act(M, K, case=case, tensor=0, row_lognormal=row_lognormal,
+                  outlier_mult=act_outlier)
+    w = synth.weight(N, K, case=case, tensor=1)
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(a))
+    qw, sw = oracle.quant_w_128x128(synth.bf16_bits(w))
+    return qa, sa, qw, sw
+
+
+def _run(fp8bs, qa, sa, qw, sw, out_dtype):
+    c = fp8bs.fp8_block_gemm(gu.u8(qa), gu.f32(sa), gu.u8(qw), gu.f32(sw), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return c
+
+
+def test_tiny_case_end_to_end(fp8bs):
+    """Tiny workload: GPU quantizers (bit-exact) then the GEMM, fp32 output,
+    all 32,768 outputs checked."""
+    a, w = synth.tiny_inputs()
+    ab, wb = synth.bf16_bits(a), synth.bf16_bits(w)
+    qa_g, sa_g = fp8bs.fp8_quant_act_1x128(gu.bf16_from_bits(ab))
+    qw_g, sw_g = fp8bs.fp8_quant_w_128x128(gu.bf16_from_bits(wb))
+    c = fp8bs.fp8_block_gemm(qa_g, sa_g, qw_g, sw_g, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qa, sa = oracle.quant_act_1x128(ab)
+    qw, sw = oracle.quant_w_128x128(wb)
+    gu.assert_same_bits(gu.host(qa_g), qa, "A codes")
+    gu.assert_same_bits(gu.host(qw_g), qw, "W codes")
+    C, B = oracle.block_gemm(qa, sa, qw, sw)
+    gu.check_gemm(c, C, B)
+
+
+@pytest.mark.parametrize("M,N,K,out", [
+    (128, 256, 512, torch.float32),
+    (200, 300, 640, torch.bfloat16),
+    (1, 128, 128, torch.float32),
+    (257, 129, 1152, torch.bfloat16),
+    (512, 1024, 1024, torch.bfloat16),
+])
+def test_ragged_shapes(fp8bs, M, N, K, out):
+    qa, sa, qw, sw = _quantized(M, N, K, case=400 + M + N)
+    c = _run(fp8bs, qa, sa, qw, sw, out)
+    C, B = oracle.block_gemm(qa, sa, qw, sw)
+    gu.check_gemm(c, C, B)
+
+
+def test_one_hot_indexing_exact(fp8bs):
+    """A single non-zero A element at (m0, k0): row m0 of C is
+    sa*sb*dec(a)*dec(w[:, k0]) (exact in fp32), every other row is 0."""
+    qa, sa, qw, sw = _quantized(64, 384, 512, case=410)
+    m0, k0 = 37, 300
+    qa1 = np.zeros_like(qa)
+    qa1[m0, k0] = 0x45  # 3.25
+    c = gu.host(_run(fp8bs, qa1, sa, qw, sw, torch.float32))
+    tab = oracle.decode_table()
+    kb0 = k0 // 128
+    sc = np.float32(sa[kb0, m0]) * np.repeat(sw[:, kb0], 128)[:384].astype(np.float32)
+    want_row = (np.float32(3.25) * tab[qw[:, k0]].astype(np.float32)) * sc
+    want = np.zeros_like(c)
+    want[m0] = want_row.astype(np.float32)
+    # product of exact partial (3.25 * w) and the fp32 scale product: one rounding
+    gu.assert_same_bits(c, want, "one-hot output")
+
+
+def test_power_of_two_scale_metamorphic(fp8bs):
+    """Scaling every activation scale by 2^j scales the fp32 output by 2^j
+    exactly."""
+    qa, sa, qw, sw = _quantized(256, 256, 768, case=411)
+    c0 = gu.host(_run(fp8bs, qa, sa, qw, sw, torch.float32))
+    for j in (-7, 9):
+        cj = gu.host(_run(fp8bs, qa, (sa * np.float32(2.0 ** j)).astype(np.float32), qw, sw,
+                          torch.float32))
+        gu.assert_same_bits(cj, (c0 * np.float32(2.0 ** j)).astype(np.float32), f"2^{j}")
+
+
+def test_promotion_adversary(fp8bs):
+    """Per-group scales spanning 2^+-20 inside one row: only per-group FP32
+    promotion meets the tolerance."""
+    qa, sa, qw, sw = _quantized(64, 256, 1024, case=412)
+    rng = np.random.default_rng(412)
+    sa = (sa * np.float32(2.0) ** rng.integers(-20, 21, sa.shape)).astype(np.float32)
+    sw = (sw * np.float32(2.0) ** rng.integers(-20, 21, sw.shape)).astype(np.float32)
+    c = _run(fp8bs, qa, sa, qw, sw, torch.float32)
+    C, B = oracle.block_gemm(qa, sa, qw, sw)
+    gu.check_gemm(c, C, B)
+
+
+def test_identity_scale_plain_matmul(fp8bs):
+    """E4M3-representable inputs with every group maximum at 448: the GEMM is
+    a plain matmul of the inputs."""
+    rng = np.random.default_rng(413)
+    tab = oracle.decode_table()
+    finite = tab[[c for c in range(256) if c not in (0x7F, 0xFF)]]
+    M, N, K = 128, 256, 384
+    a = rng.choice(finite, (M, K))
+    w = rng.choice(finite, (N, K))
+    a[:, ::128] = 448.0
+    w[::128, :] = -448.0
+    qa = oracle.encode(a.astype(np.float32))
+    qw = oracle.encode(w.astype(np.float32))
+    sa = np.ones((K // 128, M), np.float32)
+    sw = np.ones((N // 128, K // 128), np.float32)
+    c = gu.host_f64(_run(fp8bs, qa, sa, qw, sw, torch.float32))
+    ref = a @ w.T
+    B = np.abs(a) @ np.abs(w).T
+    gu.check_gemm(c, ref, B)
+
+
+def test_strided_operands_and_output(fp8bs):
+    qa, sa, qw, sw = _quantized(96, 256, 512, case=414)
+    A = torch.zeros(96, 640, dtype=torch.uint8, device="cuda")
+    A[:, :512] = gu.u8(qa)
+    SA = torch.zeros(4, 112, dtype=torch.float32, device="cuda")
+    SA[:, :96] = gu.f32(sa)
+    OUT = torch.full((96, 272), -1.0, dtype=torch.float32, device="cuda")
+    fp8bs.fp8_block_gemm(A[:, :512], SA, gu.u8(qw), gu.f32(sw), out=OUT[:, :256])
+    torch.cuda.synchronize()
+    C, B = oracle.block_gemm(qa, sa, qw, sw)
+    gu.check_gemm(OUT[:, :256], C, B)
+    assert torch.all(OUT[:, 256:] == -1.0)
+
+
+def test_full_size_dense_sampled(fp8bs):
+    """Dense workload at full size (M=4096, N=18432, K=7168, bf16 out, the
+    launch the benchmark times): GPU quantizers then the GEMM; sampled rows x
+    sampled 128-column blocks are checked against the oracle run on the same
+    bf16 inputs (codes of the sampled rows and bands are also compared)."""
+    M, N, K = 4096, 18432, 7168
+    a = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
+    w = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
+    qa_g, sa_g = fp8bs.fp8_quant_act_1x128(a)
+    qw_g, sw_g = fp8bs.fp8_quant_w_128x128(w)
+    c = fp8bs.fp8_block_gemm(qa_g, sa_g, qw_g, sw_g, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.array(sorted(set([0, 127, 128, 255, 4095] + rng.choice(M, 27, replace=False).tolist())))
+    bands = np.array(sorted(set([0, 143] + rng.choice(144, 14, replace=False).tolist())))
+    ab = synth.bf16_bits(a[torch.from_numpy(rows).cuda()])
+    qa, sa = oracle.quant_act_1x128(ab)
+    gu.assert_same_bits(gu.host(qa_g)[rows], qa, "sampled A codes")
+    gu.assert_same_bits(gu.host(sa_g)[:, rows], sa, "sampled A scales")
+    wb_all = w.view(N // 128, 128, K)
+    ch = gu.host_f64(c)
+    worst = 0.0
+    for nb in bands:
+        qw, sw = oracle.quant_w_128x128(synth.bf16_bits(wb_all[nb]))
+        gu.assert_same_bits(gu.host(qw_g[nb * 128:(nb + 1) * 128]), qw, f"band {nb} codes")
+        C, B = oracle.block_gemm(qa, sa, qw, sw)
+        worst = max(worst, gu.check_gemm(ch[rows][:, nb * 128:(nb + 1) * 128], C, B,
+                                          bf16=True))
+    print(f"dense full-size sampled: worst err/bound = {worst:.4f}")

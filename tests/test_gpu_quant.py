@@ -1,0 +1,141 @@
+"""GPU parity of the online quantizers: codes and scales must equal the
+oracle's bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_05_amd import synth
+from tests import _gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp8bs():
+    from fp8_block_scaled_05_amd import fp8bs as mod
+    return mod
+
+
+def _act_case(fp8bs, bits, lds=None):
+    x = gu.bf16_from_bits(bits)
+    q, s = fp8bs.fp8_quant_act_1x128(x, lds=lds)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_act_1x128(bits)
+    M = bits.shape[0]
+    gu.assert_same_bits(gu.host(q), qr, "act codes")
+    gu.assert_same_bits(gu.host(s)[:, :M], sr, "act scales")
+    return q, s
+
+
+def _w_case(fp8bs, bits):
+    w = gu.bf16_from_bits(bits)
+    q, s = fp8bs.fp8_quant_w_128x128(w)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_w_128x128(bits)
+    gu.assert_same_bits(gu.host(q), qr, "weight codes")
+    gu.assert_same_bits(gu.host(s), sr, "weight scales")
+
+
+def test_tiny_case_bit_exact(fp8bs):
+    a, w = synth.tiny_inputs()
+    _act_case(fp8bs, synth.bf16_bits(a))
+    _w_case(fp8bs, synth.bf16_bits(w))
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (63, 256), (1000, 1024), (4099, 384)])
+def test_act_ragged_rows(fp8bs, M, K):
+    x = synth.act(M, K, case=100 + M, tensor=0)
+    _act_case(fp8bs, synth.bf16_bits(x))
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (130, 256), (300, 768), (1024, 512)])
+def test_weight_ragged_bands(fp8bs, N, K):
+    w = synth.weight(N, K, case=200 + N, tensor=1)
+    _w_case(fp8bs, synth.bf16_bits(w))
+
+
+def test_act_strided_input_and_scales(fp8bs):
+    full = synth.act(100, 512, case=300, tensor=0)
+    x = gu.bf16_from_bits(synth.bf16_bits(full))[:, 128:384]  # ldx = 512, K = 256
+    q, s = fp8bs.fp8_quant_act_1x128(x, lds=104)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_act_1x128(synth.bf16_bits(full)[:, 128:384])
+    gu.assert_same_bits(gu.host(q), qr, "codes")
+    gu.assert_same_bits(gu.host(s)[:, :100], sr, "scales")
+
+
+def _all_bf16_up_to_448():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits[np.isfinite(f) & (np.abs(f) <= 448.0)]
+
+
+def test_hardware_convert_every_bf16_value(fp8bs):
+    """Tiles whose maximum is exactly 448 have s = r = 1, so each code is the
+    E4M3 encoding of the input itself: this runs every finite bf16 value with
+    |x| <= 448 (including subnormals, ties and signed zero) through the GPU
+    convert."""
+    vals = _all_bf16_up_to_448()
+    per = 127
+    rows = -(-len(vals) // per)
+    tile = np.zeros((rows, 128), dtype=np.uint16)
+    flat = np.zeros(rows * per, dtype=np.uint16)
+    flat[:len(vals)] = vals
+    tile[:, :per] = flat.reshape(rows, per)
+    tile[:, per] = 0x43E0  # 448.0
+    q, s = _act_case(fp8bs, tile)
+    assert np.all(gu.host(s) == 1.0)
+
+
+def test_edge_tiles(fp8bs):
+    """Zero, signed-zero, subnormal-only, +-448 and single-outlier tiles."""
+    t = np.zeros((8, 128), dtype=np.uint16)
+    t[1, :] = 0x8000                                   # all -0
+    t[2, :] = np.arange(128, dtype=np.uint16) % 0x7F + 1  # bf16 subnormals
+    t[3, ::2] = 0x43E0                                 # 448
+    t[3, 1::2] = 0xC3E0                                # -448
+    t[4, :] = 0x3F80                                   # all 1.0
+    t[4, 77] = 0x4B80                                  # 2^24 outlier
+    t[5, :] = 0x0001                                   # smallest subnormal
+    t[5, 3] = 0x8001
+    t[6, :] = 0x7F7F                                   # largest finite bf16
+    t[7, :] = 0xFF7F
+    _act_case(fp8bs, t)
+    _w_case(fp8bs, np.tile(t, (32, 1)))
+
+
+def test_deterministic_repeat(fp8bs):
+    x = gu.bf16_from_bits(synth.bf16_bits(synth.act(512, 1024, case=301, tensor=0)))
+    q1, s1 = fp8bs.fp8_quant_act_1x128(x)
+    q2, s2 = fp8bs.fp8_quant_act_1x128(x)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def test_full_size_activation_8192x7168(fp8bs):
+    """The quantizer workload at full size (all 58.7M codes and 458,752
+    scales checked)."""
+    x = synth.act(8192, 7168, case=synth.QUANT.case_id, tensor=0, device="cuda")
+    q, s = fp8bs.fp8_quant_act_1x128(x)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_act_1x128(synth.bf16_bits(x))
+    gu.assert_same_bits(gu.host(q), qr, "codes")
+    gu.assert_same_bits(gu.host(s), sr, "scales")
+
+
+def test_full_size_weight_18432x7168_sampled_bands(fp8bs):
+    """The weight workload at full size; every block of 24 sampled 128-row
+    bands (plus the first and last) is checked."""
+    w = synth.weight(18432, 7168, case=synth.QUANT.case_id, tensor=1, device="cuda")
+    q, s = fp8bs.fp8_quant_w_128x128(w)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    bands = sorted(set([0, 143] + rng.choice(144, 24, replace=False).tolist()))
+    wb = synth.bf16_bits(w)
+    qh, sh = gu.host(q), gu.host(s)
+    for nb in bands:
+        qr, sr = oracle.quant_w_128x128(wb[nb * 128:(nb + 1) * 128])
+        gu.assert_same_bits(qh[nb * 128:(nb + 1) * 128], qr, f"band {nb} codes")
+        gu.assert_same_bits(sh[nb:nb + 1], sr, f"band {nb} scales")
