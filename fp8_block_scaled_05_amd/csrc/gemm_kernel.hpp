@@ -1,0 +1,433 @@
+// Block-scaled FP8 GEMM kernel template for gfx950 (dense and grouped/MoE).
+//
+// C = A . B^T with E4M3 operands.  For every 128-wide K group kb the kernel
+// forms the FP8 x FP8 partial product of that group in FP32 (one
+// V_MFMA_F32_16X16X128_F8F6F4 covers a 16x16 output tile's whole group) and
+// promotes it into the FP32 running sum with one multiply-add by
+// S_A(m,kb) * S_W(n/128,kb).  Pages: "Advantages of using FP8 for GEMM
+// operations in DeepSeek-V3", items 1, 5 and 8 (FP8 GEMM for dense and MoE
+// layers; partial results promoted to FP32 registers at fixed intervals of
+// the accumulation); "How the unified E4M3 format adds to DeepSeek-V3's
+// efficiency", section "Enhanced numerical stability".  The promotion
+// interval is the 128-K group, where the scales change.
+//
+// Structure: WM x WN waves per BM x BN output tile; each wave owns a
+// (BM/WM) x (BN/WN) sub-tile made of 16x16 MFMA tiles.  Every K group of A,
+// B, the activation scales and the weight-block scales is copied HBM->LDS by
+// direct buffer_load ... lds (no register staging) into one of STAGES LDS
+// buffers; STAGES-1 groups are in flight while one feeds the MFMAs.  LDS rows
+// are 128 bytes; the eight 16-byte chunks of a row are stored XOR-swizzled
+// (lds_swizzle) so that the fragment reads are free of bank conflicts.  The lane K order inside an MFMA operand (32 bytes = chunks 2g, 2g+1
+// for lane group g) is the same for A and B, so products pair matching K.
+// Within a group the MFMAs of tile-row i are issued before the FP32
+// promotion of tile-row i-1, so the VALU multiply-adds overlap the matrix
+// cores.
+#pragma once
+
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace fp8bs {
+namespace gemm {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS placement of the eight 16-byte K chunks of a 128-byte tile row: chunk c
+// of row r is stored in slot c ^ lds_swizzle(r).  The function depends on
+// r mod 16 only, so the MFMA reads (16 consecutive rows per fragment) can
+// compute it from the lane index; with it the ds_read_b128 fragment reads of
+// a wave are free of LDS bank conflicts on gfx950 (measured with
+// SQ_LDS_BANK_CONFLICT; plain r & 7 or (r >> 1) & 7 leave 2-way conflicts).
+__device__ __forceinline__ int lds_swizzle(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int GROUP_M_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int STAGES = STAGES_, GROUP_M = GROUP_M_;
+  static constexpr int NWAVES = WM * WN, THREADS = 64 * NWAVES;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
+  static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 MFMA tiles per wave
+  // LDS stage: A rows | B rows | activation scales | weight-block scales | pad
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = BM * 128;
+  static constexpr int SA_OFF = B_OFF + BN * 128;
+  static constexpr int SB_OFF = SA_OFF + BM * 4;
+  static constexpr int DUMMY_OFF = SB_OFF + 64 * 4;
+  static constexpr int STAGE_BYTES = DUMMY_OFF + 64 * 4;
+  // 1 KB (8 rows) per wave-wide direct load
+  static constexpr int TILE_LOADS = (BM + BN) / 8 / NWAVES;
+  // scale loads: BM/64 for S_A, one for S_W, padded so every wave issues the
+  // same number per stage (the vmcnt bookkeeping is then wave-independent)
+  static constexpr int SCALE_LOADS = (BM / 64 + 1 + NWAVES - 1) / NWAVES;
+  static constexpr int LOADS = TILE_LOADS + SCALE_LOADS;
+  static_assert((BM + BN) / 8 % NWAVES == 0, "tile loads must split evenly over waves");
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave sub-tile must be whole MFMA tiles");
+  static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns must share one weight block");
+  static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 LDS stages");
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LOADS <= 63, "vmcnt range");
+};
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct TileCoords {
+  int64_t row0, row_end, col0;
+  const uint8_t* b;
+  const float* sb;
+};
+
+template <class C, bool GROUPED>
+__device__ __forceinline__ bool tile_coords(const GemmArgs& p, TileCoords& t) {
+  const int64_t KB = p.K / 128;
+  const int64_t NB = (p.N + 127) / 128;
+  const int64_t NT = (p.N + C::BN - 1) / C::BN;
+  const int64_t MT = GROUPED ? (p.M + C::BM - 1) / C::BM + p.G : (p.M + C::BM - 1) / C::BM;
+  // Workgroups are dealt round-robin to the 8 XCDs: give each XCD a
+  // contiguous run of tiles, and inside it walk GROUP_M tile-rows before
+  // moving along N so that concurrently resident tiles share A and B in L2.
+  int64_t bid = blockIdx.x;
+  const int64_t T = (int64_t)gridDim.x;
+  if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
+  const int64_t per_group = (int64_t)C::GROUP_M * NT;
+  const int64_t first_m = (bid / per_group) * C::GROUP_M;
+  const int64_t gsz = (MT - first_m) < C::GROUP_M ? (MT - first_m) : C::GROUP_M;
+  const int64_t in_grp = bid % per_group;
+  const int64_t tm = first_m + in_grp % gsz;
+  const int64_t tn = in_grp / gsz;
+  t.col0 = tn * C::BN;
+  t.b = p.b;
+  t.sb = p.sb;
+  if constexpr (GROUPED) {
+    const int32_t* __restrict__ off = p.group_offsets;
+    int64_t seen = 0, g = -1, local = 0;
+    for (int64_t gg = 0; gg < p.G; ++gg) {
+      const int64_t cnt = ((int64_t)off[gg + 1] - off[gg] + C::BM - 1) / C::BM;
+      if (tm < seen + cnt) {
+        g = gg;
+        local = tm - seen;
+        break;
+      }
+      seen += cnt;
+    }
+    if (g < 0) return false;  // past the last real tile
+    t.row0 = off[g] + local * C::BM;
+    t.row_end = off[g + 1];
+    t.b += g * p.b_group_stride;
+    t.sb += g * NB * KB;
+  } else {
+    t.row0 = tm * C::BM;
+    t.row_end = p.M;
+  }
+  return true;
+}
+
+// Loop-invariant per-lane byte offsets of one stage's direct copies,
+// relative to wave-uniform bases (so each copy needs one 32-bit VGPR).
+template <class C>
+struct LoadPlan {
+  uint32_t tile[C::TILE_LOADS];
+  uint32_t scale[C::SCALE_LOADS];
+};
+
+template <class C>
+__device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t, int wave,
+                                          int lane, LoadPlan<C>& lp) {
+  const int64_t KB = p.K / 128;
+  const int64_t NB = (p.N + 127) / 128;
+  const int rows_a = (int)(t.row_end - t.row0);       // >= 1
+  const int rows_b = (int)(p.N - t.col0);             // >= 1
+#pragma unroll
+  for (int j = 0; j < C::TILE_LOADS; ++j) {
+    const int rbase = (wave * C::TILE_LOADS + j) * 8;  // first of 8 rows, A then B
+    const int r = rbase + (lane >> 3);
+    const int chunk = (lane & 7) ^ lds_swizzle(r);
+    if (rbase < C::BM) {
+      const int rr = r < rows_a ? r : rows_a - 1;
+      lp.tile[j] = (uint32_t)rr * (uint32_t)p.lda + chunk * 16;
+    } else {
+      const int rr = (r - C::BM) < rows_b ? (r - C::BM) : rows_b - 1;
+      lp.tile[j] = (uint32_t)rr * (uint32_t)p.ldb + chunk * 16;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < C::SCALE_LOADS; ++s) {
+    const int id = wave + s * C::NWAVES;
+    if (id < C::BM / 64) {
+      const int rr = id * 64 + lane < rows_a ? id * 64 + lane : rows_a - 1;
+      lp.scale[s] = (uint32_t)rr * 4;
+    } else {
+      const int64_t nbl = NB - 1 - t.col0 / 128;       // last block index within the tile
+      const int nb = lane < nbl ? lane : (int)nbl;
+      lp.scale[s] = (uint32_t)(nb * KB) * 4;
+    }
+  }
+}
+
+// Buffer resources (base + byte range in SGPRs) of the tile's A rows, B rows,
+// activation scales and weight-block scales.  Offsets never leave the range:
+// rows past the edge are clamped to the last valid row.
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t a, b, sa, sb;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  // raw (stride 0) buffer over [base, base + 4 GiB); 0x00020000 is the
+  // gfx9 word-3 setting for untyped dword access
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0xFFFFFFFF,
+                                           0x00020000);
+}
+
+template <class C>
+__device__ __forceinline__ Rsrc make_rsrc_set(const GemmArgs& p, const TileCoords& t) {
+  const int64_t KB = p.K / 128;
+  Rsrc r;
+  r.a = make_rsrc(p.a + t.row0 * p.lda);
+  r.b = make_rsrc(t.b + t.col0 * p.ldb);
+  r.sa = make_rsrc(p.sa + t.row0);
+  r.sb = make_rsrc(t.sb + (t.col0 / 128) * KB);
+  return r;
+}
+
+// Issue copy number `idx` (0 <= idx < LOADS) of K group kb into one stage.
+// Copies 0..SCALE_LOADS-1 bring the scales (the same count on every wave:
+// S_A for 64 rows, the tile's S_W blocks, or a repeat into a never-read slot),
+// the rest bring 1 KB blocks (8 rows x 128 B) of A and then B.
+template <class C>
+__device__ __forceinline__ void issue_copy(const GemmArgs& p, const Rsrc& rs,
+                                           const LoadPlan<C>& lp, int64_t kb, uint8_t* st,
+                                           int wave, int idx) {
+  if (idx < C::SCALE_LOADS) {
+    const int id = wave + idx * C::NWAVES;
+    const bool is_sa = id < C::BM / 64;
+    const int dst = is_sa ? C::SA_OFF + id * 256 : (id == C::BM / 64 ? C::SB_OFF : C::DUMMY_OFF);
+    const int soff = is_sa ? (int)(kb * p.ldsa * 4) : (int)(kb * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_sa ? rs.sa : rs.sb, (lds_void*)(st + dst), 4,
+                                             lp.scale[idx], soff, 0, 0);
+  } else {
+    const int j = idx - C::SCALE_LOADS;
+    const int rbase = (wave * C::TILE_LOADS + j) * 8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rbase < C::BM ? rs.a : rs.b,
+                                             (lds_void*)(st + rbase * 128), 16, lp.tile[j],
+                                             (int)(kb * 128), 0, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void issue_stage(const GemmArgs& p, const Rsrc& rs,
+                                            const LoadPlan<C>& lp, int64_t kb, uint8_t* st,
+                                            int wave) {
+#pragma unroll
+  for (int idx = 0; idx < C::LOADS; ++idx) issue_copy<C>(p, rs, lp, kb, st, wave, idx);
+}
+
+// Two 16-byte LDS reads -> one 32-byte MFMA operand (K chunks 2g, 2g+1).
+__device__ __forceinline__ v8i load_frag(const uint8_t* rowp, int slot0) {
+  const int4 lo = *reinterpret_cast<const int4*>(rowp + slot0 * 16);
+  const int4 hi = *reinterpret_cast<const int4*>(rowp + (slot0 ^ 1) * 16);
+  return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// One K group from one LDS stage.  The wave's FM x FN MFMAs are issued in
+// row-major order into a ring of RING partial products; the FP32 promotion
+// of the MFMA issued RING steps earlier (long finished) follows each issue,
+// so the VALU multiply-adds overlap the matrix cores.  The next stage's
+// copies are spread between the MFMA rows (a burst of them would stall the
+// wave at issue while the load pipe drains).
+template <class C, bool REFILL, class Refill>
+__device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[C::FM][C::FN],
+                                              int wm, int wn, int lane,
+                                              Refill&& issue_copy_n) {
+  constexpr int NM = C::FM * C::FN;
+  constexpr int RING = 4;
+  static_assert(C::FN + 1 > RING, "scale registers of a row are reused two rows later");
+  constexpr int PER_ROW = (C::LOADS + C::FM - 1) / C::FM;
+  const int l16 = lane & 15;
+  // rows r (r mod 16 == l16) and the K chunk pair 2g, 2g+1 of lane group
+  // g = lane / 16; chunk c of row r sits in slot c ^ lds_swizzle(r)
+  const int slot0 = (2 * (lane >> 4)) ^ lds_swizzle(l16);
+  const uint8_t* arow = st + C::A_OFF + (wm * C::TM + l16) * 128;
+  const uint8_t* brow = st + C::B_OFF + (wn * C::TN + l16) * 128;
+  const float sbv = reinterpret_cast<const float*>(st + C::SB_OFF)[(wn * C::TN) / 128];
+  const float* sa = reinterpret_cast<const float*>(st + C::SA_OFF) + wm * C::TM + 4 * (lane >> 4);
+  v8i bf[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) bf[j] = load_frag(brow + 16 * j * 128, slot0);
+  v8i af[2];
+  float4 s4[2];
+  float w[2][4];
+  af[0] = load_frag(arow, slot0);
+  s4[0] = *reinterpret_cast<const float4*>(sa);
+  v4f ring[RING];
+#pragma unroll
+  for (int t = 0; t < NM + RING; ++t) {
+    if (t >= RING) {
+      const int u = t - RING, i = u / C::FN, j = u % C::FN;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[i][j][r] = __builtin_fmaf(ring[u % RING][r], w[i & 1][r], acc[i][j][r]);
+    }
+    if (t < NM) {
+      const int i = t / C::FN, j = t % C::FN;
+      if (j == 0) {
+        // this row's promotion factors S_A(row) * S_W; prefetch the next row
+        w[i & 1][0] = s4[i & 1].x * sbv;
+        w[i & 1][1] = s4[i & 1].y * sbv;
+        w[i & 1][2] = s4[i & 1].z * sbv;
+        w[i & 1][3] = s4[i & 1].w * sbv;
+        if (i + 1 < C::FM) {
+          af[(i + 1) & 1] = load_frag(arow + 16 * (i + 1) * 128, slot0);
+          s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(sa + 16 * (i + 1));
+        }
+      }
+      ring[t % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          af[i & 1], bf[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      if (j == C::FN - 1 && REFILL) {
+#pragma unroll
+        for (int c = i * PER_ROW; c < (i + 1) * PER_ROW && c < C::LOADS; ++c) issue_copy_n(c);
+      }
+    }
+  }
+  // scheduling pattern for this region: 1 MFMA, then up to 5 VALU, repeated
+#pragma unroll
+  for (int t = 0; t < NM; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Keep this group's promotion inside this step: without a use here the
+  // compiler sinks the multiply-adds past the next barrier, which piles two
+  // groups' VALU work into one step.
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) asm volatile("" : "+v"(acc[i][j]));
+}
+
+template <class C, bool GROUPED, bool OUT_BF16>
+__device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[C::STAGES > 2 ? C::STAGE_BYTES : 16];
+
+  TileCoords t;
+  if (!tile_coords<C, GROUPED>(p, t)) return;  // whole workgroup
+
+  // wave index in an SGPR so that per-wave values stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int64_t KB = p.K / 128;
+
+  LoadPlan<C> lp;
+  make_plan<C>(p, t, wave, lane, lp);
+  const Rsrc rs = make_rsrc_set<C>(p, t);
+
+  v4f acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Pipeline: group g lives in LDS stage g % STAGES.  Step kb waits for this
+  // wave's copies of group kb (leaving the copies of later groups in flight),
+  // meets the other waves at a barrier (so every copy of group kb is visible
+  // and every wave has finished reading the stage about to be refilled),
+  // refills that stage with group kb + STAGES - 1, then computes group kb.
+  // The steady-state loop always refills; the last steps are peeled.
+  auto stg = [&](int i) -> uint8_t* { return i == 0 ? st0 : (i == 1 ? st1 : st2); };
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < KB) issue_stage<C>(p, rs, lp, s, stg(s), wave);
+
+  auto wait_and_sync = [&](bool later_in_flight) {
+    if (later_in_flight) {
+      wait_vmcnt<C::LOADS * (C::STAGES - 2)>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+  };
+
+  int64_t kb = 0;
+  // steady state: STAGES steps per iteration, each refilling the stage read
+  // in the previous step with copies interleaved into its MFMA stream
+  for (; kb + 2 * C::STAGES - 2 < KB; kb += C::STAGES) {
+#pragma unroll
+    for (int u = 0; u < C::STAGES; ++u) {
+      wait_and_sync(C::STAGES > 2);
+      uint8_t* const nxt = stg((u + C::STAGES - 1) % C::STAGES);
+      const int64_t kn = kb + u + C::STAGES - 1;
+      compute_stage<C, true>(stg(u), acc, wm, wn, lane, [&](int c) {
+        issue_copy<C>(p, rs, lp, kn, nxt, wave, c);
+      });
+    }
+  }
+  // drain: at most 2*STAGES-2 steps remain; unrolled so stage indices stay
+  // compile-time constants; any refill is issued before the compute
+#pragma unroll
+  for (int u = 0; u < 2 * C::STAGES - 2; ++u) {
+    const int64_t k = kb + u;
+    if (k < KB) {
+      wait_and_sync(C::STAGES > 2 && k + C::STAGES - 2 < KB);
+      if (k + C::STAGES - 1 < KB)
+        issue_stage<C>(p, rs, lp, k + C::STAGES - 1, stg((u + C::STAGES - 1) % C::STAGES), wave);
+      compute_stage<C, false>(stg(u % C::STAGES), acc, wm, wn, lane, [](int) {});
+    }
+  }
+
+  // Epilogue: a lane holds rows 4*(lane/16) + r, column lane%16 of each
+  // 16x16 tile.
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int64_t col = t.col0 + wn * C::TN + 16 * j + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = t.row0 + wm * C::TM + 16 * i + 4 * g4 + r;
+        if (row < t.row_end && col < p.N) {
+          if constexpr (OUT_BF16) {
+            reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+          } else {
+            reinterpret_cast<float*>(p.c)[row * p.ldc + col] = acc[i][j][r];
+          }
+        }
+      }
+    }
+  }
+}
+
+// The buffer-resource type exists only for the device; the host pass sees an
+// empty kernel (it only needs the launch stub).
+template <class C, bool GROUPED, bool OUT_BF16>
+__global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  block_gemm_body<C, GROUPED, OUT_BF16>(p);
+#endif
+}
+
+template <class C, bool GROUPED>
+hipError_t launch(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
+  const int64_t NT = (args.N + C::BN - 1) / C::BN;
+  const int64_t MT =
+      GROUPED ? (args.M + C::BM - 1) / C::BM + args.G : (args.M + C::BM - 1) / C::BM;
+  const int64_t blocks = MT * NT;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (out_bf16) {
+    hipLaunchKernelGGL((block_gemm_kernel<C, GROUPED, true>), dim3((unsigned)blocks),
+                       dim3(C::THREADS), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((block_gemm_kernel<C, GROUPED, false>), dim3((unsigned)blocks),
+                       dim3(C::THREADS), 0, stream, args);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gemm
+}  // namespace fp8bs
