@@ -15,13 +15,14 @@
 // (BM/WM) x (BN/WN) sub-tile made of 16x16 MFMA tiles.  Every K group of A,
 // B, the activation scales and the weight-block scales is copied HBM->LDS by
 // direct buffer_load ... lds (no register staging) into one of STAGES LDS
-// buffers; STAGES-1 groups are in flight while one feeds the MFMAs.  LDS rows
-// are 128 bytes; the eight 16-byte chunks of a row are stored XOR-swizzled
-// (lds_swizzle) so that the fragment reads are free of bank conflicts.  The lane K order inside an MFMA operand (32 bytes = chunks 2g, 2g+1
-// for lane group g) is the same for A and B, so products pair matching K.
-// Within a group the MFMAs of tile-row i are issued before the FP32
-// promotion of tile-row i-1, so the VALU multiply-adds overlap the matrix
-// cores.
+// buffers; STAGES-1 groups are in flight while one feeds the MFMAs, and the
+// copies of the next group are spread between the MFMA rows.  LDS rows are
+// 128 bytes; the eight 16-byte chunks of a row are stored XOR-swizzled
+// (lds_swizzle) so that the fragment reads are free of bank conflicts.  The
+// lane K order inside an MFMA operand (32 bytes = chunks 2g, 2g+1 for lane
+// group g) is the same for A and B, so products pair matching K.  Each
+// MFMA's FP32 promotion is issued a few MFMAs later (a ring of partial
+// products), so the VALU multiply-adds overlap the matrix cores.
 #pragma once
 
 #include "device.hpp"
@@ -47,23 +48,27 @@ struct Cfg {
   static constexpr int NWAVES = WM * WN, THREADS = 64 * NWAVES;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 MFMA tiles per wave
-  // LDS stage: A rows | B rows | activation scales | weight-block scales | pad
+  // weight-block scales of the tile: one per 128 columns
+  static constexpr int SB_COUNT = (BN + 127) / 128;
+  // LDS stage: A rows | B rows; the scales of a stage live in a separate
+  // array (activation scales, then weight-block scales) so that the compiler
+  // can tell their register->LDS writes from the in-flight tile copies
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * 128;
-  static constexpr int SA_OFF = B_OFF + BN * 128;
-  static constexpr int SB_OFF = SA_OFF + BM * 4;
-  static constexpr int DUMMY_OFF = SB_OFF + 64 * 4;
-  static constexpr int STAGE_BYTES = DUMMY_OFF + 64 * 4;
+  static constexpr int STAGE_BYTES = B_OFF + BN * 128;
   // 1 KB (8 rows) per wave-wide direct load
   static constexpr int TILE_LOADS = (BM + BN) / 8 / NWAVES;
-  // scale loads: BM/64 for S_A, one for S_W, padded so every wave issues the
-  // same number per stage (the vmcnt bookkeeping is then wave-independent)
-  static constexpr int SCALE_LOADS = (BM / 64 + 1 + NWAVES - 1) / NWAVES;
-  static constexpr int LOADS = TILE_LOADS + SCALE_LOADS;
+  // the scales go through registers (one fp32 per thread per item) and are
+  // written to LDS after the compute; SREG loads per thread per stage
+  static constexpr int SCALE_ITEMS = BM + SB_COUNT;
+  static constexpr int SREG = (SCALE_ITEMS + THREADS - 1) / THREADS;
+  // every thread writes its SREG slots (no branch, so no merged wait counts)
+  static constexpr int SCALE_FLOATS = SREG * THREADS;
+  static constexpr int LOADS = TILE_LOADS + SREG;  // vector-memory ops per wave per stage
   static_assert((BM + BN) / 8 % NWAVES == 0, "tile loads must split evenly over waves");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave sub-tile must be whole MFMA tiles");
   static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns must share one weight block");
-  static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 LDS stages");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS <= 63, "vmcnt range");
 };
@@ -73,6 +78,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier after this wave's LDS writes (lgkmcnt) and all but its
+// last N vector-memory ops have completed.  __syncthreads() would also wait
+// for every direct-to-LDS copy still in flight (its release fence covers
+// them), which would drain the copy pipeline at every K group; the memory
+// clobber keeps the compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void barrier_after_vmcnt() {
+  wait_vmcnt<N>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 struct TileCoords {
@@ -131,7 +147,7 @@ __device__ __forceinline__ bool tile_coords(const GemmArgs& p, TileCoords& t) {
 template <class C>
 struct LoadPlan {
   uint32_t tile[C::TILE_LOADS];
-  uint32_t scale[C::SCALE_LOADS];
+  int32_t scale[C::SREG];  // element offset from the tile's S_A (or S_W) column base
 };
 
 template <class C>
@@ -139,6 +155,7 @@ __device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t
                                           int lane, LoadPlan<C>& lp) {
   const int64_t KB = p.K / 128;
   const int64_t NB = (p.N + 127) / 128;
+  (void)wave;
   const int rows_a = (int)(t.row_end - t.row0);       // >= 1
   const int rows_b = (int)(p.N - t.col0);             // >= 1
 #pragma unroll
@@ -155,15 +172,16 @@ __device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t
     }
   }
 #pragma unroll
-  for (int s = 0; s < C::SCALE_LOADS; ++s) {
-    const int id = wave + s * C::NWAVES;
-    if (id < C::BM / 64) {
-      const int rr = id * 64 + lane < rows_a ? id * 64 + lane : rows_a - 1;
-      lp.scale[s] = (uint32_t)rr * 4;
+  for (int s = 0; s < C::SREG; ++s) {
+    const int item = (int)threadIdx.x + s * C::THREADS;
+    if (item < C::BM) {
+      lp.scale[s] = item < rows_a ? item : rows_a - 1;
     } else {
-      const int64_t nbl = NB - 1 - t.col0 / 128;       // last block index within the tile
-      const int nb = lane < nbl ? lane : (int)nbl;
-      lp.scale[s] = (uint32_t)(nb * KB) * 4;
+      // weight-block scale j of the tile (items past the end repeat the last)
+      const int64_t nbl = NB - 1 - t.col0 / 128;  // last block index within the tile
+      int j = item - C::BM;
+      j = j < C::SB_COUNT ? j : C::SB_COUNT - 1;
+      lp.scale[s] = (int)((j < nbl ? j : nbl) * KB);
     }
   }
 }
@@ -172,7 +190,7 @@ __device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t
 // activation scales and weight-block scales.  Offsets never leave the range:
 // rows past the edge are clamped to the last valid row.
 struct Rsrc {
-  __amdgpu_buffer_rsrc_t a, b, sa, sb;
+  __amdgpu_buffer_rsrc_t a, b;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
@@ -186,35 +204,48 @@ template <class C>
 __device__ __forceinline__ Rsrc make_rsrc_set(const GemmArgs& p, const TileCoords& t) {
   const int64_t KB = p.K / 128;
   Rsrc r;
+  (void)KB;
   r.a = make_rsrc(p.a + t.row0 * p.lda);
   r.b = make_rsrc(t.b + t.col0 * p.ldb);
-  r.sa = make_rsrc(p.sa + t.row0);
-  r.sb = make_rsrc(t.sb + (t.col0 / 128) * KB);
   return r;
 }
 
-// Issue copy number `idx` (0 <= idx < LOADS) of K group kb into one stage.
-// Copies 0..SCALE_LOADS-1 bring the scales (the same count on every wave:
-// S_A for 64 rows, the tile's S_W blocks, or a repeat into a never-read slot),
-// the rest bring 1 KB blocks (8 rows x 128 B) of A and then B.
+// Issue tile copy number `idx` (0 <= idx < TILE_LOADS) of K group kb into one
+// stage: a 1 KB block (8 rows x 128 B) of A, then of B.
 template <class C>
 __device__ __forceinline__ void issue_copy(const GemmArgs& p, const Rsrc& rs,
                                            const LoadPlan<C>& lp, int64_t kb, uint8_t* st,
                                            int wave, int idx) {
-  if (idx < C::SCALE_LOADS) {
-    const int id = wave + idx * C::NWAVES;
-    const bool is_sa = id < C::BM / 64;
-    const int dst = is_sa ? C::SA_OFF + id * 256 : (id == C::BM / 64 ? C::SB_OFF : C::DUMMY_OFF);
-    const int soff = is_sa ? (int)(kb * p.ldsa * 4) : (int)(kb * 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_sa ? rs.sa : rs.sb, (lds_void*)(st + dst), 4,
-                                             lp.scale[idx], soff, 0, 0);
-  } else {
-    const int j = idx - C::SCALE_LOADS;
-    const int rbase = (wave * C::TILE_LOADS + j) * 8;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rbase < C::BM ? rs.a : rs.b,
-                                             (lds_void*)(st + rbase * 128), 16, lp.tile[j],
-                                             (int)(kb * 128), 0, 0);
+  (void)p;
+  const int rbase = (wave * C::TILE_LOADS + idx) * 8;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rbase < C::BM ? rs.a : rs.b,
+                                           (lds_void*)(st + rbase * 128), 16, lp.tile[idx],
+                                           (int)(kb * 128), 0, 0);
+}
+
+// The scales of K group kb, one fp32 per item, into registers.  Issued before
+// the group's tile copies, so that waiting for them (before they are written
+// to LDS) leaves the tile copies in flight.
+template <class C>
+__device__ __forceinline__ void load_scales(const GemmArgs& p, const TileCoords& t,
+                                            const LoadPlan<C>& lp, int64_t kb,
+                                            float (&v)[C::SREG]) {
+  const int64_t KB = p.K / 128;
+  const float* sa = p.sa + kb * p.ldsa + t.row0;
+  const float* sb = t.sb + (t.col0 / 128) * KB + kb;
+#pragma unroll
+  for (int s = 0; s < C::SREG; ++s) {
+    const int item = (int)threadIdx.x + s * C::THREADS;
+    // one load instruction per item slot on every wave (uniform vmcnt counts)
+    const float* src = item < C::BM ? sa : sb;
+    v[s] = src[lp.scale[s]];
   }
+}
+
+template <class C>
+__device__ __forceinline__ void store_scales(float* sc, const float (&v)[C::SREG]) {
+#pragma unroll
+  for (int s = 0; s < C::SREG; ++s) sc[(int)threadIdx.x + s * C::THREADS] = v[s];
 }
 
 template <class C>
@@ -222,14 +253,43 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, const Rsrc& rs,
                                             const LoadPlan<C>& lp, int64_t kb, uint8_t* st,
                                             int wave) {
 #pragma unroll
-  for (int idx = 0; idx < C::LOADS; ++idx) issue_copy<C>(p, rs, lp, kb, st, wave, idx);
+  for (int idx = 0; idx < C::TILE_LOADS; ++idx) issue_copy<C>(p, rs, lp, kb, st, wave, idx);
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Per-lane LDS byte offsets of a wave's MFMA operands inside a stage (the
+// same for every stage).  They are made opaque to the optimizer once, so that
+// each fragment address is the stage base plus one register plus a constant:
+// the LDS lowering then tags every read with the stage's alias scope, and the
+// wait-count pass can tell reads of a landed stage from copies still in
+// flight to the other stages (an untagged read waits for every copy).
+struct FragOffs {
+  int a_lo, a_hi, b_lo, b_hi;  // K chunks 2g and 2g+1 of lane group g
+  int sa;                      // float index of the lane's first activation scale
+};
+
+template <class C>
+__device__ __forceinline__ FragOffs frag_offsets(int wm, int wn, int lane) {
+  const int l16 = lane & 15;
+  // rows r (r mod 16 == l16) and the K chunk pair 2g, 2g+1 of lane group
+  // g = lane / 16; chunk c of row r sits in slot c ^ lds_swizzle(r)
+  const int slot0 = (2 * (lane >> 4)) ^ lds_swizzle(l16);
+  FragOffs f;
+  f.a_lo = C::A_OFF + (wm * C::TM + l16) * 128 + slot0 * 16;
+  f.a_hi = C::A_OFF + (wm * C::TM + l16) * 128 + (slot0 ^ 1) * 16;
+  f.b_lo = C::B_OFF + (wn * C::TN + l16) * 128 + slot0 * 16;
+  f.b_hi = C::B_OFF + (wn * C::TN + l16) * 128 + (slot0 ^ 1) * 16;
+  f.sa = wm * C::TM + 4 * (lane >> 4);
+  asm volatile("" : "+v"(f.a_lo), "+v"(f.a_hi), "+v"(f.b_lo), "+v"(f.b_hi), "+v"(f.sa));
+  return f;
 }
 
 // Two 16-byte LDS reads -> one 32-byte MFMA operand (K chunks 2g, 2g+1).
-__device__ __forceinline__ v8i load_frag(const uint8_t* rowp, int slot0) {
-  const int4 lo = *reinterpret_cast<const int4*>(rowp + slot0 * 16);
-  const int4 hi = *reinterpret_cast<const int4*>(rowp + (slot0 ^ 1) * 16);
-  return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+__device__ __forceinline__ v8i load_frag(const uint8_t* st, int lo, int hi, int row_bytes) {
+  const v4i a = *reinterpret_cast<const v4i*>(st + lo + row_bytes);
+  const v4i b = *reinterpret_cast<const v4i*>(st + hi + row_bytes);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // One K group from one LDS stage.  The wave's FM x FN MFMAs are issued in
@@ -239,29 +299,24 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* rowp, int slot0) {
 // copies are spread between the MFMA rows (a burst of them would stall the
 // wave at issue while the load pipe drains).
 template <class C, bool REFILL, class Refill>
-__device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[C::FM][C::FN],
-                                              int wm, int wn, int lane,
-                                              Refill&& issue_copy_n) {
+__device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc,
+                                              const FragOffs& fo, v4f (&acc)[C::FM][C::FN],
+                                              int wn, Refill&& issue_copy_n) {
   constexpr int NM = C::FM * C::FN;
   constexpr int RING = 4;
-  static_assert(C::FN + 1 > RING, "scale registers of a row are reused two rows later");
-  constexpr int PER_ROW = (C::LOADS + C::FM - 1) / C::FM;
-  const int l16 = lane & 15;
-  // rows r (r mod 16 == l16) and the K chunk pair 2g, 2g+1 of lane group
-  // g = lane / 16; chunk c of row r sits in slot c ^ lds_swizzle(r)
-  const int slot0 = (2 * (lane >> 4)) ^ lds_swizzle(l16);
-  const uint8_t* arow = st + C::A_OFF + (wm * C::TM + l16) * 128;
-  const uint8_t* brow = st + C::B_OFF + (wn * C::TN + l16) * 128;
-  const float sbv = reinterpret_cast<const float*>(st + C::SB_OFF)[(wn * C::TN) / 128];
-  const float* sa = reinterpret_cast<const float*>(st + C::SA_OFF) + wm * C::TM + 4 * (lane >> 4);
+  // the promotion factors of row i are read until step i*FN + FN - 1 + RING
+  // and their slot is refilled at step (i + WS)*FN
+  constexpr int WS = 2 + (RING - 1) / C::FN;
+  constexpr int PER_ROW = (C::TILE_LOADS + C::FM - 1) / C::FM;
+  const float sbv = sc[C::BM + (wn * C::TN) / 128];
   v8i bf[C::FN];
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) bf[j] = load_frag(brow + 16 * j * 128, slot0);
+  for (int j = 0; j < C::FN; ++j) bf[j] = load_frag(st, fo.b_lo, fo.b_hi, 16 * j * 128);
   v8i af[2];
   float4 s4[2];
-  float w[2][4];
-  af[0] = load_frag(arow, slot0);
-  s4[0] = *reinterpret_cast<const float4*>(sa);
+  float w[WS][4];
+  af[0] = load_frag(st, fo.a_lo, fo.a_hi, 0);
+  s4[0] = *reinterpret_cast<const float4*>(sc + fo.sa);
   v4f ring[RING];
 #pragma unroll
   for (int t = 0; t < NM + RING; ++t) {
@@ -269,26 +324,26 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[C::F
       const int u = t - RING, i = u / C::FN, j = u % C::FN;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        acc[i][j][r] = __builtin_fmaf(ring[u % RING][r], w[i & 1][r], acc[i][j][r]);
+        acc[i][j][r] = __builtin_fmaf(ring[u % RING][r], w[i % WS][r], acc[i][j][r]);
     }
     if (t < NM) {
       const int i = t / C::FN, j = t % C::FN;
       if (j == 0) {
         // this row's promotion factors S_A(row) * S_W; prefetch the next row
-        w[i & 1][0] = s4[i & 1].x * sbv;
-        w[i & 1][1] = s4[i & 1].y * sbv;
-        w[i & 1][2] = s4[i & 1].z * sbv;
-        w[i & 1][3] = s4[i & 1].w * sbv;
+        w[i % WS][0] = s4[i & 1].x * sbv;
+        w[i % WS][1] = s4[i & 1].y * sbv;
+        w[i % WS][2] = s4[i & 1].z * sbv;
+        w[i % WS][3] = s4[i & 1].w * sbv;
         if (i + 1 < C::FM) {
-          af[(i + 1) & 1] = load_frag(arow + 16 * (i + 1) * 128, slot0);
-          s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(sa + 16 * (i + 1));
+          af[(i + 1) & 1] = load_frag(st, fo.a_lo, fo.a_hi, 16 * (i + 1) * 128);
+          s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(sc + fo.sa + 16 * (i + 1));
         }
       }
       ring[t % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           af[i & 1], bf[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
       if (j == C::FN - 1 && REFILL) {
 #pragma unroll
-        for (int c = i * PER_ROW; c < (i + 1) * PER_ROW && c < C::LOADS; ++c) issue_copy_n(c);
+        for (int c = i * PER_ROW; c < (i + 1) * PER_ROW && c < C::TILE_LOADS; ++c) issue_copy_n(c);
       }
     }
   }
@@ -313,6 +368,11 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t st1[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t st2[C::STAGES > 2 ? C::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[C::STAGES > 3 ? C::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) float sc0[C::SCALE_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sc1[C::SCALE_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sc2[C::STAGES > 2 ? C::SCALE_FLOATS : 4];
+  __shared__ __attribute__((aligned(16))) float sc3[C::STAGES > 3 ? C::SCALE_FLOATS : 4];
 
   TileCoords t;
   if (!tile_coords<C, GROUPED>(p, t)) return;  // whole workgroup
@@ -325,6 +385,7 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
 
   LoadPlan<C> lp;
   make_plan<C>(p, t, wave, lane, lp);
+  const FragOffs fo = frag_offsets<C>(wm, wn, lane);
   const Rsrc rs = make_rsrc_set<C>(p, t);
 
   v4f acc[C::FM][C::FN];
@@ -339,17 +400,38 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
   // and every wave has finished reading the stage about to be refilled),
   // refills that stage with group kb + STAGES - 1, then computes group kb.
   // The steady-state loop always refills; the last steps are peeled.
-  auto stg = [&](int i) -> uint8_t* { return i == 0 ? st0 : (i == 1 ? st1 : st2); };
-  for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < KB) issue_stage<C>(p, rs, lp, s, stg(s), wave);
+  auto stg = [&](int i) -> uint8_t* {
+    return i == 0 ? st0 : (i == 1 ? st1 : (i == 2 ? st2 : st3));
+  };
+  auto scl = [&](int i) -> float* {
+    return i == 0 ? sc0 : (i == 1 ? sc1 : (i == 2 ? sc2 : sc3));
+  };
+  // group g lives in stage g % STAGES; the scales of a group are loaded to
+  // registers with its tile copies and written to its stage afterwards.
+  // Every prologue stage is filled (with the last group again when KB is
+  // smaller than STAGES - 1; such a stage is never read): a conditional fill
+  // would make the compiler assume, at the top of the steady loop, that
+  // stage 0 may still be in flight.  The extra copies are issued after every
+  // real group, so the drain's waits (which count real groups only) still
+  // cover them.
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s) {
+    const int64_t g = s < KB ? s : KB - 1;
+    float sv[C::SREG];
+    load_scales<C>(p, t, lp, g, sv);
+    issue_stage<C>(p, rs, lp, g, stg(s), wave);
+    store_scales<C>(scl(s), sv);
+  }
 
-  auto wait_and_sync = [&](bool later_in_flight) {
-    if (later_in_flight) {
-      wait_vmcnt<C::LOADS * (C::STAGES - 2)>();
+  // wait until at most `later` groups (issued after group kb) are in flight
+  auto wait_and_sync = [&](int later) {
+    if (C::STAGES > 3 && later >= 2) {
+      barrier_after_vmcnt<C::LOADS * (C::STAGES > 3 ? 2 : 0)>();
+    } else if (C::STAGES > 2 && later >= 1) {
+      barrier_after_vmcnt<C::LOADS * (C::STAGES > 2 ? 1 : 0)>();
     } else {
-      wait_vmcnt<0>();
+      barrier_after_vmcnt<0>();
     }
-    __syncthreads();
   };
 
   int64_t kb = 0;
@@ -358,12 +440,18 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
   for (; kb + 2 * C::STAGES - 2 < KB; kb += C::STAGES) {
 #pragma unroll
     for (int u = 0; u < C::STAGES; ++u) {
-      wait_and_sync(C::STAGES > 2);
+      wait_and_sync(C::STAGES - 2);
       uint8_t* const nxt = stg((u + C::STAGES - 1) % C::STAGES);
       const int64_t kn = kb + u + C::STAGES - 1;
-      compute_stage<C, true>(stg(u), acc, wm, wn, lane, [&](int c) {
+      float sv[C::SREG];
+      load_scales<C>(p, t, lp, kn, sv);
+      // keep the scale loads ahead of this step's tile copies (in-order
+      // completion then lets store_scales wait for them alone)
+      __builtin_amdgcn_sched_barrier(0);
+      compute_stage<C, true>(stg(u), scl(u), fo, acc, wn, [&](int c) {
         issue_copy<C>(p, rs, lp, kn, nxt, wave, c);
       });
+      store_scales<C>(scl((u + C::STAGES - 1) % C::STAGES), sv);
     }
   }
   // drain: at most 2*STAGES-2 steps remain; unrolled so stage indices stay
@@ -372,10 +460,17 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
   for (int u = 0; u < 2 * C::STAGES - 2; ++u) {
     const int64_t k = kb + u;
     if (k < KB) {
-      wait_and_sync(C::STAGES > 2 && k + C::STAGES - 2 < KB);
-      if (k + C::STAGES - 1 < KB)
-        issue_stage<C>(p, rs, lp, k + C::STAGES - 1, stg((u + C::STAGES - 1) % C::STAGES), wave);
-      compute_stage<C, false>(stg(u % C::STAGES), acc, wm, wn, lane, [](int) {});
+      const int64_t last = k + C::STAGES - 2 < KB - 1 ? k + C::STAGES - 2 : KB - 1;
+      wait_and_sync((int)(last - k));
+      uint8_t* const nxt = stg((u + C::STAGES - 1) % C::STAGES);
+      const bool refill = k + C::STAGES - 1 < KB;
+      float sv[C::SREG];
+      if (refill) {
+        load_scales<C>(p, t, lp, k + C::STAGES - 1, sv);
+        issue_stage<C>(p, rs, lp, k + C::STAGES - 1, nxt, wave);
+      }
+      compute_stage<C, false>(stg(u % C::STAGES), scl(u % C::STAGES), fo, acc, wn, [](int) {});
+      if (refill) store_scales<C>(scl((u + C::STAGES - 1) % C::STAGES), sv);
     }
   }
 
