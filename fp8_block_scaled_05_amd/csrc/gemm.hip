@@ -1,4 +1,13 @@
 // Launchers of the block-scaled FP8 GEMM (kernel template in gemm_kernel.hpp).
+//
+// Tile shapes by problem shape (measured on MI355X with the dense, grouped and
+// few-row workloads):
+// - large M: 128x256 tiles, 8 waves of 64x64, three LDS stages (two K groups
+//   in flight while one is consumed); the same shape serves the grouped path,
+//   whose per-expert row counts are ragged;
+// - few rows (decode-like, weight-bandwidth bound): short tiles so that the
+//   weight matrix is spread over many workgroups and every weight byte is
+//   read once; 1 wave along M.
 
 #include "gemm_kernel.hpp"
 
@@ -6,16 +15,21 @@ namespace fp8bs {
 
 namespace {
 // BM, BN, waves along M, waves along N, LDS stages, tile-rows per L2 group
-using DenseCfg = gemm::Cfg<256, 256, 2, 4, 2, 8>;
-using GroupedCfg = gemm::Cfg<128, 128, 2, 2, 2, 8>;
+using LargeCfg = gemm::Cfg<128, 256, 2, 4, 3, 8>;
+using Rows16Cfg = gemm::Cfg<16, 64, 1, 2, 3, 1>;
+using Rows32Cfg = gemm::Cfg<32, 64, 1, 4, 3, 1>;
+using Rows64Cfg = gemm::Cfg<64, 128, 1, 4, 3, 1>;
 }  // namespace
 
 hipError_t launch_block_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
-  return gemm::launch<DenseCfg, false>(args, out_bf16, stream);
+  if (args.M <= 16) return gemm::launch<Rows16Cfg, false>(args, out_bf16, stream);
+  if (args.M <= 32) return gemm::launch<Rows32Cfg, false>(args, out_bf16, stream);
+  if (args.M <= 64) return gemm::launch<Rows64Cfg, false>(args, out_bf16, stream);
+  return gemm::launch<LargeCfg, false>(args, out_bf16, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
-  return gemm::launch<GroupedCfg, true>(args, out_bf16, stream);
+  return gemm::launch<LargeCfg, true>(args, out_bf16, stream);
 }
 
 }  // namespace fp8bs
