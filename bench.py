@@ -14,7 +14,11 @@ path: the activation and weight quantizers alone at 8192x7168 / 18432x7168
 in-call activation quantization (M = 16, 64), and the CPU oracle on a bounded
 sample of the dense step (``cpu_baseline``).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-parts]
+The default 300 warm-up steps (about 0.2 s) bring the engine clock to its
+sustained level before the timed steps; with only a few warm-up steps the
+first timed GEMMs run at a lower clock.
+
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 300] [--no-parts]
        [--no-cpu-baseline]
 """
 
@@ -41,8 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_dense_gemm_M4096_N184
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-parts", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()

@@ -2,9 +2,12 @@
 //
 // Tile shapes by problem shape (measured on MI355X with the dense, grouped and
 // few-row workloads):
-// - large M: 128x256 tiles, 8 waves of 64x64, three LDS stages (two K groups
-//   in flight while one is consumed); the same shape serves the grouped path,
-//   whose per-expert row counts are ragged;
+// - large M: 256x256 tiles, 8 waves of 128x64, two LDS stages (128 KB); the
+//   large tile halves the L2->LDS traffic per flop compared with 128x256,
+//   which matters more than the deeper pipeline a smaller tile would allow;
+//   the same shape serves the grouped path.  When the dense raster would end
+//   in a partial round of workgroups, its last tiles run as pairs of
+//   128x256 tiles (a half-length last round);
 // - few rows (decode-like, weight-bandwidth bound): short tiles so that the
 //   weight matrix is spread over many workgroups and every weight byte is
 //   read once; 1 wave along M.
@@ -15,7 +18,9 @@ namespace fp8bs {
 
 namespace {
 // BM, BN, waves along M, waves along N, LDS stages, tile-rows per L2 group
-using LargeCfg = gemm::Cfg<128, 256, 2, 4, 3, 8>;
+using LargeCfg = gemm::Cfg<256, 256, 2, 4, 2, 4>;
+// half-height tiles for a last partial round of the dense raster
+using LargeTail = gemm::Cfg<128, 256, 2, 4, 2, 4>;
 using Rows16Cfg = gemm::Cfg<16, 64, 1, 2, 3, 1>;
 using Rows32Cfg = gemm::Cfg<32, 64, 1, 4, 3, 1>;
 using Rows64Cfg = gemm::Cfg<64, 128, 1, 4, 3, 1>;
@@ -25,7 +30,7 @@ hipError_t launch_block_gemm(const GemmArgs& args, bool out_bf16, hipStream_t st
   if (args.M <= 16) return gemm::launch<Rows16Cfg, false>(args, out_bf16, stream);
   if (args.M <= 32) return gemm::launch<Rows32Cfg, false>(args, out_bf16, stream);
   if (args.M <= 64) return gemm::launch<Rows64Cfg, false>(args, out_bf16, stream);
-  return gemm::launch<LargeCfg, false>(args, out_bf16, stream);
+  return gemm::launch<LargeCfg, false, LargeTail>(args, out_bf16, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream) {

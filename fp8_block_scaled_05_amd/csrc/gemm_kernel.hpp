@@ -97,18 +97,22 @@ struct TileCoords {
   const float* sb;
 };
 
+// Workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous
+// run of the raster (of length T) so that concurrently resident tiles of one
+// XCD share A and B in its L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t T) {
+  return T % 8 == 0 ? (bid % 8) * (T / 8) + bid / 8 : bid;
+}
+
+// Coordinates of tile number `i` of the raster, which walks GROUP_M tile-rows
+// before moving along N.  Grouped: false past the last real tile.
 template <class C, bool GROUPED>
-__device__ __forceinline__ bool tile_coords(const GemmArgs& p, TileCoords& t) {
+__device__ __forceinline__ bool tile_coords(const GemmArgs& p, int64_t i, TileCoords& t) {
   const int64_t KB = p.K / 128;
   const int64_t NB = (p.N + 127) / 128;
   const int64_t NT = (p.N + C::BN - 1) / C::BN;
   const int64_t MT = GROUPED ? (p.M + C::BM - 1) / C::BM + p.G : (p.M + C::BM - 1) / C::BM;
-  // Workgroups are dealt round-robin to the 8 XCDs: give each XCD a
-  // contiguous run of tiles, and inside it walk GROUP_M tile-rows before
-  // moving along N so that concurrently resident tiles share A and B in L2.
-  int64_t bid = blockIdx.x;
-  const int64_t T = (int64_t)gridDim.x;
-  if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
+  const int64_t bid = i;
   const int64_t per_group = (int64_t)C::GROUP_M * NT;
   const int64_t first_m = (bid / per_group) * C::GROUP_M;
   const int64_t gsz = (MT - first_m) < C::GROUP_M ? (MT - first_m) : C::GROUP_M;
@@ -307,7 +311,11 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   // the promotion factors of row i are read until step i*FN + FN - 1 + RING
   // and their slot is refilled at step (i + WS)*FN
   constexpr int WS = 2 + (RING - 1) / C::FN;
-  constexpr int PER_ROW = (C::TILE_LOADS + C::FM - 1) / C::FM;
+  // With two stages the copies of the next group must land before this
+  // step ends: issue them over the first half of the rows.  With more stages
+  // they have a whole step of slack and are spread over all rows.
+  constexpr int ISSUE_ROWS = C::STAGES == 2 ? (C::FM + 1) / 2 : C::FM;
+  constexpr int PER_ROW = (C::TILE_LOADS + ISSUE_ROWS - 1) / ISSUE_ROWS;
   const float sbv = sc[C::BM + (wn * C::TN) / 128];
   v8i bf[C::FN];
 #pragma unroll
@@ -363,20 +371,17 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
     for (int j = 0; j < C::FN; ++j) asm volatile("" : "+v"(acc[i][j]));
 }
 
-template <class C, bool GROUPED, bool OUT_BF16>
-__device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
-  __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[C::STAGES > 2 ? C::STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t st3[C::STAGES > 3 ? C::STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(16))) float sc0[C::SCALE_FLOATS];
-  __shared__ __attribute__((aligned(16))) float sc1[C::SCALE_FLOATS];
-  __shared__ __attribute__((aligned(16))) float sc2[C::STAGES > 2 ? C::SCALE_FLOATS : 4];
-  __shared__ __attribute__((aligned(16))) float sc3[C::STAGES > 3 ? C::SCALE_FLOATS : 4];
+// The LDS arrays of the kernel: one per pipeline stage for the tiles and one
+// per stage for the scales (distinct objects, so that the compiler can tell
+// the stages apart when it tracks copies in flight).
+struct LdsSet {
+  uint8_t* st[4];
+  float* sc[4];
+};
 
-  TileCoords t;
-  if (!tile_coords<C, GROUPED>(p, t)) return;  // whole workgroup
-
+template <class C, bool OUT_BF16>
+__device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoords& t,
+                                                const LdsSet& L) {
   // wave index in an SGPR so that per-wave values stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -400,12 +405,8 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
   // and every wave has finished reading the stage about to be refilled),
   // refills that stage with group kb + STAGES - 1, then computes group kb.
   // The steady-state loop always refills; the last steps are peeled.
-  auto stg = [&](int i) -> uint8_t* {
-    return i == 0 ? st0 : (i == 1 ? st1 : (i == 2 ? st2 : st3));
-  };
-  auto scl = [&](int i) -> float* {
-    return i == 0 ? sc0 : (i == 1 ? sc1 : (i == 2 ? sc2 : sc3));
-  };
+  auto stg = [&](int i) -> uint8_t* { return L.st[i]; };
+  auto scl = [&](int i) -> float* { return L.sc[i]; };
   // group g lives in stage g % STAGES; the scales of a group are loaded to
   // registers with its tile copies and written to its stage afterwards.
   // Every prologue stage is filled (with the last group again when KB is
@@ -497,29 +498,80 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p) {
   }
 }
 
+// One launch covers the raster of BM x BN tiles.  When that raster would end
+// in a partial round of workgroups (fewer tiles than compute units left for
+// the last round), its last tiles are split into two TAIL (half-height)
+// tiles each, so the last round takes half as long: workgroups
+// [0, full) take whole tiles, the rest take half tiles.  TAIL == C: no split.
 // The buffer-resource type exists only for the device; the host pass sees an
 // empty kernel (it only needs the launch stub).
-template <class C, bool GROUPED, bool OUT_BF16>
-__global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p) {
+template <class C, class TAIL, bool GROUPED, bool OUT_BF16>
+__global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int64_t full) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  block_gemm_body<C, GROUPED, OUT_BF16>(p);
+  static_assert(TAIL::THREADS == C::THREADS && TAIL::BN == C::BN && 2 * TAIL::BM == C::BM ||
+                    std::is_same<C, TAIL>::value, "tail tiles are half-height tiles");
+  constexpr int SB = C::STAGE_BYTES > TAIL::STAGE_BYTES ? C::STAGE_BYTES : TAIL::STAGE_BYTES;
+  constexpr int SF = C::SCALE_FLOATS > TAIL::SCALE_FLOATS ? C::SCALE_FLOATS : TAIL::SCALE_FLOATS;
+  constexpr int NS = C::STAGES > TAIL::STAGES ? C::STAGES : TAIL::STAGES;
+  __shared__ __attribute__((aligned(16))) uint8_t st0[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[NS > 2 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[NS > 3 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) float sc0[SF];
+  __shared__ __attribute__((aligned(16))) float sc1[SF];
+  __shared__ __attribute__((aligned(16))) float sc2[NS > 2 ? SF : 4];
+  __shared__ __attribute__((aligned(16))) float sc3[NS > 3 ? SF : 4];
+  const LdsSet L{{st0, st1, st2, st3}, {sc0, sc1, sc2, sc3}};
+  const int64_t bid = blockIdx.x;
+  TileCoords t;
+  if (bid < full) {
+    if (!tile_coords<C, GROUPED>(p, xcd_remap(bid, full), t)) return;  // whole workgroup
+    block_gemm_body<C, OUT_BF16>(p, t, L);
+  } else if constexpr (!std::is_same<C, TAIL>::value) {
+    const int64_t j = xcd_remap(bid - full, (int64_t)gridDim.x - full);
+    tile_coords<C, false>(p, full + j / 2, t);
+    t.row0 += (j & 1) * TAIL::BM;
+    if (t.row0 >= t.row_end) return;  // lower half below the last row
+    block_gemm_body<TAIL, OUT_BF16>(p, t, L);
+  }
 #endif
 }
 
-template <class C, bool GROUPED>
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <class C, bool GROUPED, class TAIL = C>
 hipError_t launch(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
   const int64_t NT = (args.N + C::BN - 1) / C::BN;
   const int64_t MT =
       GROUPED ? (args.M + C::BM - 1) / C::BM + args.G : (args.M + C::BM - 1) / C::BM;
-  const int64_t blocks = MT * NT;
-  if (blocks <= 0) return hipSuccess;
+  const int64_t tiles = MT * NT;
+  if (tiles <= 0) return hipSuccess;
+  int64_t full = tiles, blocks = tiles;
+  if (!GROUPED && !std::is_same<C, TAIL>::value) {
+    const int64_t cus = device_cus();
+    if (cus > 0 && tiles > cus && tiles % cus != 0) {
+      full = tiles / cus * cus;
+      blocks = full + 2 * (tiles - full);
+    }
+  }
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (out_bf16) {
-    hipLaunchKernelGGL((block_gemm_kernel<C, GROUPED, true>), dim3((unsigned)blocks),
-                       dim3(C::THREADS), 0, stream, args);
+    hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, true>), dim3((unsigned)blocks),
+                       dim3(C::THREADS), 0, stream, args, full);
   } else {
-    hipLaunchKernelGGL((block_gemm_kernel<C, GROUPED, false>), dim3((unsigned)blocks),
-                       dim3(C::THREADS), 0, stream, args);
+    hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, false>), dim3((unsigned)blocks),
+                       dim3(C::THREADS), 0, stream, args, full);
   }
   return hipGetLastError();
 }

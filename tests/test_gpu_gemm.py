@@ -173,3 +173,19 @@ def test_full_size_dense_sampled(fp8bs):
         worst = max(worst, gu.check_gemm(ch[rows][:, nb * 128:(nb + 1) * 128], C, B,
                                           bf16=True))
     print(f"dense full-size sampled: worst err/bound = {worst:.4f}")
+
+
+@pytest.mark.parametrize("M,NT", [(200, 257), (100, 257), (512, 129)])
+def test_last_round_split_tiles(fp8bs, M, NT):
+    """Rasters of more 256x256 tiles than compute units and not a multiple of
+    them: the last tiles run as half-height tiles (the lower one partly or
+    wholly past the last row).  Every output is checked."""
+    K = 256
+    N = NT * 256
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = ((M + 255) // 256) * NT
+    assert tiles > cus and tiles % cus != 0, "shape must leave a partial last round"
+    qa, sa, qw, sw = _quantized(M, N, K, case=420 + M)
+    c = _run(fp8bs, qa, sa, qw, sw, torch.float32)
+    C, B = oracle.block_gemm(qa, sa, qw, sw)
+    gu.check_gemm(c, C, B)
