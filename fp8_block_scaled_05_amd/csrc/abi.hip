@@ -80,6 +80,7 @@ int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa, int64_t ld
   g.M = M;
   g.N = N;
   g.K = K;
+  g.sb_ld = K / kTile;
   if (a_kind == FP8BS_A_E4M3) {
     g.a = static_cast<const uint8_t*>(a);
     g.lda = lda;
@@ -135,6 +136,7 @@ int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64
   g.M = M_total;
   g.N = N;
   g.K = K;
+  g.sb_ld = K / kTile;
   g.group_offsets = group_offsets;
   g.G = G;
   return hip_status(fp8bs::launch_grouped_gemm(g, out_kind == FP8BS_OUT_BF16,

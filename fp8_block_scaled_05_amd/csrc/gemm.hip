@@ -10,7 +10,7 @@
 //   128x256 tiles (a half-length last round);
 // - few rows (decode-like, weight-bandwidth bound): short tiles so that the
 //   weight matrix is spread over many workgroups and every weight byte is
-//   read once; 1 wave along M.
+//   read once; 1 wave along M; four LDS stages (three K groups in flight).
 
 #include "gemm_kernel.hpp"
 
@@ -21,13 +21,11 @@ namespace {
 using LargeCfg = gemm::Cfg<256, 256, 2, 4, 2, 4>;
 // half-height tiles for a last partial round of the dense raster
 using LargeTail = gemm::Cfg<128, 256, 2, 4, 2, 4>;
-using Rows16Cfg = gemm::Cfg<16, 64, 1, 2, 3, 1>;
-using Rows32Cfg = gemm::Cfg<32, 64, 1, 4, 3, 1>;
-using Rows64Cfg = gemm::Cfg<64, 128, 1, 4, 3, 1>;
+using Rows32Cfg = gemm::Cfg<32, 32, 1, 2, 4, 1>;
+using Rows64Cfg = gemm::Cfg<64, 128, 1, 4, 4, 1>;
 }  // namespace
 
 hipError_t launch_block_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
-  if (args.M <= 16) return gemm::launch<Rows16Cfg, false>(args, out_bf16, stream);
   if (args.M <= 32) return gemm::launch<Rows32Cfg, false>(args, out_bf16, stream);
   if (args.M <= 64) return gemm::launch<Rows64Cfg, false>(args, out_bf16, stream);
   return gemm::launch<LargeCfg, false, LargeTail>(args, out_bf16, stream);

@@ -58,8 +58,9 @@ struct Cfg {
   static constexpr int STAGE_BYTES = B_OFF + BN * 128;
   // 1 KB (8 rows) per wave-wide direct load
   static constexpr int TILE_LOADS = (BM + BN) / 8 / NWAVES;
-  // the scales go through registers (one fp32 per thread per item) and are
-  // written to LDS after the compute; SREG loads per thread per stage
+  // the scales go through registers (one fp32 per thread per item: the BM
+  // activation scales, then the SB_COUNT weight-block scales of the tile)
+  // and are written to LDS after the compute; SREG loads per thread per stage
   static constexpr int SCALE_ITEMS = BM + SB_COUNT;
   static constexpr int SREG = (SCALE_ITEMS + THREADS - 1) / THREADS;
   // every thread writes its SREG slots (no branch, so no merged wait counts)
@@ -108,7 +109,6 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t T) {
 // before moving along N.  Grouped: false past the last real tile.
 template <class C, bool GROUPED>
 __device__ __forceinline__ bool tile_coords(const GemmArgs& p, int64_t i, TileCoords& t) {
-  const int64_t KB = p.K / 128;
   const int64_t NB = (p.N + 127) / 128;
   const int64_t NT = (p.N + C::BN - 1) / C::BN;
   const int64_t MT = GROUPED ? (p.M + C::BM - 1) / C::BM + p.G : (p.M + C::BM - 1) / C::BM;
@@ -138,7 +138,7 @@ __device__ __forceinline__ bool tile_coords(const GemmArgs& p, int64_t i, TileCo
     t.row0 = off[g] + local * C::BM;
     t.row_end = off[g + 1];
     t.b += g * p.b_group_stride;
-    t.sb += g * NB * KB;
+    t.sb += g * NB * p.sb_ld;
   } else {
     t.row0 = tm * C::BM;
     t.row_end = p.M;
@@ -157,7 +157,6 @@ struct LoadPlan {
 template <class C>
 __device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t, int wave,
                                           int lane, LoadPlan<C>& lp) {
-  const int64_t KB = p.K / 128;
   const int64_t NB = (p.N + 127) / 128;
   (void)wave;
   const int rows_a = (int)(t.row_end - t.row0);       // >= 1
@@ -185,7 +184,7 @@ __device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t
       const int64_t nbl = NB - 1 - t.col0 / 128;  // last block index within the tile
       int j = item - C::BM;
       j = j < C::SB_COUNT ? j : C::SB_COUNT - 1;
-      lp.scale[s] = (int)((j < nbl ? j : nbl) * KB);
+      lp.scale[s] = (int)((j < nbl ? j : nbl) * p.sb_ld);
     }
   }
 }
@@ -206,9 +205,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 
 template <class C>
 __device__ __forceinline__ Rsrc make_rsrc_set(const GemmArgs& p, const TileCoords& t) {
-  const int64_t KB = p.K / 128;
   Rsrc r;
-  (void)KB;
   r.a = make_rsrc(p.a + t.row0 * p.lda);
   r.b = make_rsrc(t.b + t.col0 * p.ldb);
   return r;
@@ -234,9 +231,8 @@ template <class C>
 __device__ __forceinline__ void load_scales(const GemmArgs& p, const TileCoords& t,
                                             const LoadPlan<C>& lp, int64_t kb,
                                             float (&v)[C::SREG]) {
-  const int64_t KB = p.K / 128;
   const float* sa = p.sa + kb * p.ldsa + t.row0;
-  const float* sb = t.sb + (t.col0 / 128) * KB + kb;
+  const float* sb = t.sb + (t.col0 / 128) * p.sb_ld + kb;
 #pragma unroll
   for (int s = 0; s < C::SREG; ++s) {
     const int item = (int)threadIdx.x + s * C::THREADS;
@@ -317,6 +313,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   constexpr int ISSUE_ROWS = C::STAGES == 2 ? (C::FM + 1) / 2 : C::FM;
   constexpr int PER_ROW = (C::TILE_LOADS + ISSUE_ROWS - 1) / ISSUE_ROWS;
   const float sbv = sc[C::BM + (wn * C::TN) / 128];
+  const float* w4 = sc + fo.sa;
   v8i bf[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) bf[j] = load_frag(st, fo.b_lo, fo.b_hi, 16 * j * 128);
@@ -324,7 +321,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   float4 s4[2];
   float w[WS][4];
   af[0] = load_frag(st, fo.a_lo, fo.a_hi, 0);
-  s4[0] = *reinterpret_cast<const float4*>(sc + fo.sa);
+  s4[0] = *reinterpret_cast<const float4*>(w4);
   v4f ring[RING];
 #pragma unroll
   for (int t = 0; t < NM + RING; ++t) {
@@ -344,7 +341,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
         w[i % WS][3] = s4[i & 1].w * sbv;
         if (i + 1 < C::FM) {
           af[(i + 1) & 1] = load_frag(st, fo.a_lo, fo.a_hi, 16 * (i + 1) * 128);
-          s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(sc + fo.sa + 16 * (i + 1));
+          s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(w4 + 16 * (i + 1));
         }
       }
       ring[t % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -407,22 +404,48 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
   // The steady-state loop always refills; the last steps are peeled.
   auto stg = [&](int i) -> uint8_t* { return L.st[i]; };
   auto scl = [&](int i) -> float* { return L.sc[i]; };
-  // group g lives in stage g % STAGES; the scales of a group are loaded to
-  // registers with its tile copies and written to its stage afterwards.
+  // Group g lives in stage g % STAGES.  The scales of group g are loaded to
+  // registers with its tile copies (at step g - STAGES + 1) but written to
+  // the stage's scale array only at the end of step g - 1: a register ring of
+  // SLEAD = STAGES - 2 scale sets gives their loads the same slack as the
+  // tile copies (without it, short steps wait for the scale loads).
   // Every prologue stage is filled (with the last group again when KB is
   // smaller than STAGES - 1; such a stage is never read): a conditional fill
   // would make the compiler assume, at the top of the steady loop, that
   // stage 0 may still be in flight.  The extra copies are issued after every
   // real group, so the drain's waits (which count real groups only) still
   // cover them.
+  constexpr int SLEAD = C::STAGES - 2;
+  float carry[SLEAD > 0 ? SLEAD : 1][C::SREG];
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s) {
     const int64_t g = s < KB ? s : KB - 1;
     float sv[C::SREG];
     load_scales<C>(p, t, lp, g, sv);
     issue_stage<C>(p, rs, lp, g, stg(s), wave);
-    store_scales<C>(scl(s), sv);
+    if (s == 0) {
+      store_scales<C>(scl(0), sv);
+    } else {
+#pragma unroll
+      for (int r = 0; r < C::SREG; ++r) carry[s - 1][r] = sv[r];
+    }
   }
+  // end of the step of group k (stage index u = k % STAGES): write the scales
+  // of group k + 1, then shift the ring (cur: the scales loaded this step,
+  // group k + STAGES - 1)
+  auto retire_scales = [&](int u, const float (&cur)[C::SREG], bool store_next) {
+    if constexpr (SLEAD == 0) {
+      if (store_next) store_scales<C>(scl((u + 1) % C::STAGES), cur);
+    } else {
+      if (store_next) store_scales<C>(scl((u + 1) % C::STAGES), carry[0]);
+#pragma unroll
+      for (int d = 0; d + 1 < SLEAD; ++d)
+#pragma unroll
+        for (int r = 0; r < C::SREG; ++r) carry[d][r] = carry[d + 1][r];
+#pragma unroll
+      for (int r = 0; r < C::SREG; ++r) carry[SLEAD - 1][r] = cur[r];
+    }
+  };
 
   // wait until at most `later` groups (issued after group kb) are in flight
   auto wait_and_sync = [&](int later) {
@@ -447,12 +470,12 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
       float sv[C::SREG];
       load_scales<C>(p, t, lp, kn, sv);
       // keep the scale loads ahead of this step's tile copies (in-order
-      // completion then lets store_scales wait for them alone)
+      // completion then lets their wait leave the tile copies in flight)
       __builtin_amdgcn_sched_barrier(0);
       compute_stage<C, true>(stg(u), scl(u), fo, acc, wn, [&](int c) {
         issue_copy<C>(p, rs, lp, kn, nxt, wave, c);
       });
-      store_scales<C>(scl((u + C::STAGES - 1) % C::STAGES), sv);
+      retire_scales(u, sv, true);
     }
   }
   // drain: at most 2*STAGES-2 steps remain; unrolled so stage indices stay
@@ -466,12 +489,14 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
       uint8_t* const nxt = stg((u + C::STAGES - 1) % C::STAGES);
       const bool refill = k + C::STAGES - 1 < KB;
       float sv[C::SREG];
+#pragma unroll
+      for (int r = 0; r < C::SREG; ++r) sv[r] = 0.f;
       if (refill) {
         load_scales<C>(p, t, lp, k + C::STAGES - 1, sv);
         issue_stage<C>(p, rs, lp, k + C::STAGES - 1, nxt, wave);
       }
       compute_stage<C, false>(stg(u % C::STAGES), scl(u % C::STAGES), fo, acc, wn, [](int) {});
-      if (refill) store_scales<C>(scl((u + C::STAGES - 1) % C::STAGES), sv);
+      retire_scales(u % C::STAGES, sv, SLEAD == 0 ? refill : k + 1 < KB);
     }
   }
 

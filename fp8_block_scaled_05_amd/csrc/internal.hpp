@@ -15,6 +15,7 @@ struct GemmArgs {
   int64_t ldb;
   int64_t b_group_stride;  // bytes between experts' weights (grouped only)
   const float* sb;
+  int64_t sb_ld;  // floats between consecutive 128-row bands of S_W (= K/128 of the whole GEMM)
   void* c;
   int64_t ldc;
   int64_t M;  // rows (dense) or M_total (grouped)
