@@ -267,6 +267,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 struct FragOffs {
   int a_lo, a_hi, b_lo, b_hi;  // K chunks 2g and 2g+1 of lane group g
   int sa;                      // float index of the lane's first activation scale
+  int sv;                      // float index of the scales this lane loads for its row of 16
 };
 
 template <class C>
@@ -281,7 +282,19 @@ __device__ __forceinline__ FragOffs frag_offsets(int wm, int wn, int lane) {
   f.b_lo = C::B_OFF + (wn * C::TN + l16) * 128 + slot0 * 16;
   f.b_hi = C::B_OFF + (wn * C::TN + l16) * 128 + (slot0 ^ 1) * 16;
   f.sa = wm * C::TM + 4 * (lane >> 4);
-  asm volatile("" : "+v"(f.a_lo), "+v"(f.a_hi), "+v"(f.b_lo), "+v"(f.b_hi), "+v"(f.sa));
+  // Lanes 16g..16g+15 need the activation scales of rows 16 i + 4 g + r
+  // (i < FM, r < 4) of the wave's sub-tile: value v = 4 i + r.  With FM a
+  // multiple of 4, lane 16g + k loads values v = PV k .. PV k + PV - 1
+  // (PV = FM / 4 consecutive rows), which the rows' lanes fetch by DPP.
+  if constexpr (C::FM % 4 == 0) {
+    constexpr int PV = C::FM / 4;
+    const int v0 = PV * l16;
+    f.sv = f.sa + 16 * (v0 / 4) + v0 % 4;
+  } else {
+    f.sv = f.sa;
+  }
+  asm volatile("" : "+v"(f.a_lo), "+v"(f.a_hi), "+v"(f.b_lo), "+v"(f.b_hi), "+v"(f.sa),
+               "+v"(f.sv));
   return f;
 }
 
@@ -314,6 +327,22 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   constexpr int PER_ROW = (C::TILE_LOADS + ISSUE_ROWS - 1) / ISSUE_ROWS;
   const float sbv = sc[C::BM + (wn * C::TN) / 128];
   const float* w4 = sc + fo.sa;
+  // FM % 4 == 0: each lane holds PV of its row's activation scales (one LDS
+  // read per group instead of one 16-byte read per MFMA row) and the
+  // promotion factors take them by DPP row broadcast
+  constexpr bool DPPS = C::FM % 4 == 0;
+  constexpr int PV = DPPS ? C::FM / 4 : 1;
+  float sv[PV];
+  if constexpr (DPPS) {
+    if constexpr (PV == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(sc + fo.sv);
+      sv[0] = v.x;
+      sv[1] = v.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < PV; ++q) sv[q] = sc[fo.sv + q];
+    }
+  }
   v8i bf[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) bf[j] = load_frag(st, fo.b_lo, fo.b_hi, 16 * j * 128);
@@ -321,7 +350,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   float4 s4[2];
   float w[WS][4];
   af[0] = load_frag(st, fo.a_lo, fo.a_hi, 0);
-  s4[0] = *reinterpret_cast<const float4*>(w4);
+  if constexpr (!DPPS) s4[0] = *reinterpret_cast<const float4*>(w4);
   v4f ring[RING];
 #pragma unroll
   for (int t = 0; t < NM + RING; ++t) {
@@ -335,13 +364,23 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
       const int i = t / C::FN, j = t % C::FN;
       if (j == 0) {
         // this row's promotion factors S_A(row) * S_W; prefetch the next row
-        w[i % WS][0] = s4[i & 1].x * sbv;
-        w[i % WS][1] = s4[i & 1].y * sbv;
-        w[i % WS][2] = s4[i & 1].z * sbv;
-        w[i % WS][3] = s4[i & 1].w * sbv;
+        if constexpr (DPPS) {
+          // row 16 i + 4 g + r: value v = 4 i + r, held by lane v / PV (slot v % PV)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = 4 * i + r;
+            w[i % WS][r] = row_bcast_k(v / PV, sv[v % PV]) * sbv;
+          }
+        } else {
+          w[i % WS][0] = s4[i & 1].x * sbv;
+          w[i % WS][1] = s4[i & 1].y * sbv;
+          w[i % WS][2] = s4[i & 1].z * sbv;
+          w[i % WS][3] = s4[i & 1].w * sbv;
+        }
         if (i + 1 < C::FM) {
           af[(i + 1) & 1] = load_frag(st, fo.a_lo, fo.a_hi, 16 * (i + 1) * 128);
-          s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(w4 + 16 * (i + 1));
+          if constexpr (!DPPS)
+            s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(w4 + 16 * (i + 1));
         }
       }
       ring[t % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
