@@ -306,11 +306,10 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* st, int lo, int hi, int 
 }
 
 // One K group from one LDS stage.  The wave's FM x FN MFMAs are issued in
-// row-major order into a ring of RING partial products; the FP32 promotion
-// of the MFMA issued RING steps earlier (long finished) follows each issue,
-// so the VALU multiply-adds overlap the matrix cores.  The next stage's
-// copies are spread between the MFMA rows (a burst of them would stall the
-// wave at issue while the load pipe drains).
+// row-major order; the FP32 promotion of the MFMA issued RING steps earlier
+// (long finished) follows each issue, so the VALU multiply-adds overlap the
+// matrix cores.  The next stage's copies are spread between the MFMA rows (a
+// burst of them would stall the wave at issue while the load pipe drains).
 template <class C, bool REFILL, class Refill>
 __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc,
                                               const FragOffs& fo, v4f (&acc)[C::FM][C::FN],
@@ -390,14 +389,13 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
         for (int c = i * PER_ROW; c < (i + 1) * PER_ROW && c < C::TILE_LOADS; ++c) issue_copy_n(c);
       }
     }
+    // One scheduling region per MFMA.  The partial products are separate
+    // values, so without a fence the scheduler places each promotion right
+    // after the MFMA that produces it (register pressure is lower there),
+    // which stalls the wave on the MFMA latency (hazard NOPs); fenced, the
+    // promotion stays RING MFMAs behind its producer.
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // scheduling pattern for this region: 1 MFMA, then up to 5 VALU, repeated
-#pragma unroll
-  for (int t = 0; t < NM; ++t) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
   // Keep this group's promotion inside this step: without a use here the
   // compiler sinks the multiply-adds past the next barrier, which piles two
   // groups' VALU work into one step.
