@@ -175,6 +175,18 @@ def test_full_size_dense_sampled(fp8bs):
     print(f"dense full-size sampled: worst err/bound = {worst:.4f}")
 
 
+@pytest.mark.parametrize("M", [1, 31, 32, 33, 63, 64, 65])
+def test_few_row_tile_boundaries(fp8bs, M):
+    """E4M3 A with few rows: the row counts around the switches between the
+    short-tile configurations (32, 64) and the large tiles, N ragged; every
+    output is checked."""
+    N, K = 300, 640
+    qa, sa, qw, sw = _quantized(M, N, K, case=430 + M)
+    c = _run(fp8bs, qa, sa, qw, sw, torch.bfloat16)
+    C, B = oracle.block_gemm(qa, sa, qw, sw)
+    gu.check_gemm(c, C, B)
+
+
 @pytest.mark.parametrize("M,NT", [(200, 257), (100, 257), (512, 129)])
 def test_last_round_split_tiles(fp8bs, M, NT):
     """Rasters of more 256x256 tiles than compute units and not a multiple of

@@ -40,6 +40,7 @@ def _run(fp8bs, qa, sa, qw, sw, offsets, out_dtype):
     ([127, 1, 130, 0, 256], 384, 512, torch.bfloat16),
     ([0, 0, 300], 200, 384, torch.bfloat16),
     ([1] * 40, 128, 256, torch.float32),
+    ([513, 0, 256, 257, 1], 640, 384, torch.bfloat16),
 ])
 def test_grouped_all_outputs(fp8bs, sizes, N, K, out):
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
