@@ -7,7 +7,8 @@
 //   which matters more than the deeper pipeline a smaller tile would allow;
 //   the same shape serves the grouped path.  When the dense raster would end
 //   in a partial round of workgroups, its last tiles run as pairs of
-//   128x256 tiles (a half-length last round);
+//   128x256 tiles (a half-length last round); a group whose last tile-row
+//   holds at most 128 rows runs that row as 128x256 tiles;
 // - few rows (decode-like, weight-bandwidth bound): short tiles so that the
 //   weight matrix is spread over many workgroups and every weight byte is
 //   read once; 1 wave along M; four LDS stages (three K groups in flight).
@@ -19,7 +20,8 @@ namespace fp8bs {
 namespace {
 // BM, BN, waves along M, waves along N, LDS stages, tile-rows per L2 group
 using LargeCfg = gemm::Cfg<256, 256, 2, 4, 2, 4>;
-// half-height tiles for a last partial round of the dense raster
+// half-height tiles: a last partial round of the dense raster, and groups'
+// last tile-rows of at most 128 rows
 using LargeTail = gemm::Cfg<128, 256, 2, 4, 2, 4>;
 using Rows32Cfg = gemm::Cfg<32, 32, 1, 2, 4, 1>;
 using Rows64Cfg = gemm::Cfg<64, 128, 1, 4, 4, 1>;
@@ -32,7 +34,7 @@ hipError_t launch_block_gemm(const GemmArgs& args, bool out_bf16, hipStream_t st
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
-  return gemm::launch<LargeCfg, true>(args, out_bf16, stream);
+  return gemm::launch<LargeCfg, true, LargeTail>(args, out_bf16, stream);
 }
 
 }  // namespace fp8bs

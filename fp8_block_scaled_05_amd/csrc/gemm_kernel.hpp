@@ -98,52 +98,95 @@ struct TileCoords {
   const float* sb;
 };
 
-// Workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous
-// run of the raster (of length T) so that concurrently resident tiles of one
-// XCD share A and B in its L2.
+// Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+// b mod 8): give each XCD a contiguous run of the raster of T tiles (the
+// first T mod 8 XCDs one tile more than the others), so that concurrently
+// resident tiles of one XCD share A and B in its L2.  A bijection of [0, T).
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t T) {
-  return T % 8 == 0 ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  const int64_t x = bid % 8, q = T / 8, r = T % 8;
+  return x * q + (x < r ? x : r) + bid / 8;
 }
 
-// Coordinates of tile number `i` of the raster, which walks GROUP_M tile-rows
-// before moving along N.  Grouped: false past the last real tile.
-template <class C, bool GROUPED>
-__device__ __forceinline__ bool tile_coords(const GemmArgs& p, int64_t i, TileCoords& t) {
-  const int64_t NB = (p.N + 127) / 128;
+// Coordinates of tile number `i` of a raster with MT tile-rows, which walks
+// GROUP_M tile-rows before moving along N: tile-row tm, first column col0.
+template <class C>
+__device__ __forceinline__ void raster(const GemmArgs& p, int64_t i, int64_t MT, int64_t& tm,
+                                       int64_t& col0) {
   const int64_t NT = (p.N + C::BN - 1) / C::BN;
-  const int64_t MT = GROUPED ? (p.M + C::BM - 1) / C::BM + p.G : (p.M + C::BM - 1) / C::BM;
-  const int64_t bid = i;
   const int64_t per_group = (int64_t)C::GROUP_M * NT;
-  const int64_t first_m = (bid / per_group) * C::GROUP_M;
+  const int64_t first_m = (i / per_group) * C::GROUP_M;
   const int64_t gsz = (MT - first_m) < C::GROUP_M ? (MT - first_m) : C::GROUP_M;
-  const int64_t in_grp = bid % per_group;
-  const int64_t tm = first_m + in_grp % gsz;
-  const int64_t tn = in_grp / gsz;
-  t.col0 = tn * C::BN;
+  const int64_t in_grp = i % per_group;
+  tm = first_m + in_grp % gsz;
+  col0 = (in_grp / gsz) * C::BN;
+}
+
+template <class C>
+__device__ __forceinline__ void dense_tile(const GemmArgs& p, int64_t i, TileCoords& t) {
+  int64_t tm;
+  raster<C>(p, i, (p.M + C::BM - 1) / C::BM, tm, t.col0);
   t.b = p.b;
   t.sb = p.sb;
-  if constexpr (GROUPED) {
-    const int32_t* __restrict__ off = p.group_offsets;
-    int64_t seen = 0, g = -1, local = 0;
-    for (int64_t gg = 0; gg < p.G; ++gg) {
-      const int64_t cnt = ((int64_t)off[gg + 1] - off[gg] + C::BM - 1) / C::BM;
-      if (tm < seen + cnt) {
-        g = gg;
-        local = tm - seen;
-        break;
-      }
-      seen += cnt;
-    }
-    if (g < 0) return false;  // past the last real tile
-    t.row0 = off[g] + local * C::BM;
-    t.row_end = off[g + 1];
-    t.b += g * p.b_group_stride;
-    t.sb += g * NB * p.sb_ld;
-  } else {
-    t.row0 = tm * C::BM;
-    t.row_end = p.M;
+  t.row0 = tm * C::BM;
+  t.row_end = p.M;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, (unsigned)d, 64);
+    v += lane >= d ? u : 0;
   }
-  return true;
+  return v;
+}
+
+// Grouped raster: group g owns ceil(M_g / BM) tile-rows, in group order.
+// The offsets are scanned 64 groups at a time by the whole wave (every wave
+// of the workgroup computes the same, uniform, result).
+template <class C>
+__device__ __forceinline__ int group_row_tiles(const GemmArgs& p, int64_t g) {
+  return g < p.G ? (p.group_offsets[g + 1] - p.group_offsets[g] + C::BM - 1) / C::BM : 0;
+}
+
+// Total tile-rows over all groups.
+template <class C>
+__device__ __forceinline__ int64_t grouped_row_tiles(const GemmArgs& p) {
+  const int lane = threadIdx.x & 63;
+  int64_t total = 0;
+  for (int64_t base = 0; base < p.G; base += 64)
+    total += __builtin_amdgcn_readlane(wave_incl_sum(group_row_tiles<C>(p, base + lane)), 63);
+  return total;
+}
+
+// Tile `i` of the grouped raster with MT (the total) tile-rows.
+template <class C>
+__device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t i, int64_t MT,
+                                             TileCoords& t) {
+  const int64_t NB = (p.N + 127) / 128;
+  const int lane = threadIdx.x & 63;
+  int64_t tm;
+  raster<C>(p, i, MT, tm, t.col0);
+  // find the group holding tile-row tm (< MT, so the loop always finds it)
+  int64_t seen = 0, g = 0, local = 0;
+  for (int64_t base = 0; base < p.G; base += 64) {
+    const int cnt = group_row_tiles<C>(p, base + lane);
+    const int incl = wave_incl_sum(cnt);
+    const int64_t chunk = __builtin_amdgcn_readlane(incl, 63);
+    if (tm < seen + chunk) {
+      const unsigned long long m = __ballot(seen + incl > tm);
+      const int first = __builtin_ctzll(m);
+      g = base + first;
+      local = tm - seen - __builtin_amdgcn_readlane(incl - cnt, first);
+      break;
+    }
+    seen += chunk;
+  }
+  t.row0 = p.group_offsets[g] + local * C::BM;
+  t.row_end = p.group_offsets[g + 1];
+  t.b = p.b + g * p.b_group_stride;
+  t.sb = p.sb + g * NB * p.sb_ld;
 }
 
 // Loop-invariant per-lane byte offsets of one stage's direct copies,
@@ -560,11 +603,15 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
   }
 }
 
-// One launch covers the raster of BM x BN tiles.  When that raster would end
-// in a partial round of workgroups (fewer tiles than compute units left for
-// the last round), its last tiles are split into two TAIL (half-height)
-// tiles each, so the last round takes half as long: workgroups
-// [0, full) take whole tiles, the rest take half tiles.  TAIL == C: no split.
+// One launch covers the raster of BM x BN tiles.
+// Dense: when the raster would end in a partial round of workgroups (fewer
+// tiles than compute units left for the last round), its last tiles are
+// split into two TAIL (half-height) tiles each, so the last round takes half
+// as long: workgroups [0, full) take whole tiles, the rest take half tiles.
+// Grouped: the grid is an upper bound on the tile count (the group sizes live
+// on the device); the workgroups past the real count exit at once, and a
+// group's last tile-row runs as a TAIL tile when it holds at most TAIL::BM
+// rows.  TAIL == C: no half tiles.
 // The buffer-resource type exists only for the device; the host pass sees an
 // empty kernel (it only needs the launch stub).
 template <class C, class TAIL, bool GROUPED, bool OUT_BF16>
@@ -575,6 +622,7 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
   constexpr int SB = C::STAGE_BYTES > TAIL::STAGE_BYTES ? C::STAGE_BYTES : TAIL::STAGE_BYTES;
   constexpr int SF = C::SCALE_FLOATS > TAIL::SCALE_FLOATS ? C::SCALE_FLOATS : TAIL::SCALE_FLOATS;
   constexpr int NS = C::STAGES > TAIL::STAGES ? C::STAGES : TAIL::STAGES;
+  constexpr bool HALVES = !std::is_same<C, TAIL>::value;
   __shared__ __attribute__((aligned(16))) uint8_t st0[SB];
   __shared__ __attribute__((aligned(16))) uint8_t st1[SB];
   __shared__ __attribute__((aligned(16))) uint8_t st2[NS > 2 ? SB : 16];
@@ -586,15 +634,30 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
   const LdsSet L{{st0, st1, st2, st3}, {sc0, sc1, sc2, sc3}};
   const int64_t bid = blockIdx.x;
   TileCoords t;
-  if (bid < full) {
-    if (!tile_coords<C, GROUPED>(p, xcd_remap(bid, full), t)) return;  // whole workgroup
+  if constexpr (GROUPED) {
+    (void)full;
+    const int64_t MT = grouped_row_tiles<C>(p);
+    const int64_t T = MT * ((p.N + C::BN - 1) / C::BN);
+    if (bid >= T) return;  // whole workgroup: past the last real tile
+    grouped_tile<C>(p, xcd_remap(bid, T), MT, t);
+    if constexpr (HALVES) {
+      if (t.row_end - t.row0 <= TAIL::BM) {
+        block_gemm_body<TAIL, OUT_BF16>(p, t, L);
+        return;
+      }
+    }
     block_gemm_body<C, OUT_BF16>(p, t, L);
-  } else if constexpr (!std::is_same<C, TAIL>::value) {
-    const int64_t j = xcd_remap(bid - full, (int64_t)gridDim.x - full);
-    tile_coords<C, false>(p, full + j / 2, t);
-    t.row0 += (j & 1) * TAIL::BM;
-    if (t.row0 >= t.row_end) return;  // lower half below the last row
-    block_gemm_body<TAIL, OUT_BF16>(p, t, L);
+  } else {
+    if (bid < full) {
+      dense_tile<C>(p, xcd_remap(bid, full), t);
+      block_gemm_body<C, OUT_BF16>(p, t, L);
+    } else if constexpr (HALVES) {
+      const int64_t j = xcd_remap(bid - full, (int64_t)gridDim.x - full);
+      dense_tile<C>(p, full + j / 2, t);
+      t.row0 += (j & 1) * TAIL::BM;
+      if (t.row0 >= t.row_end) return;  // lower half below the last row
+      block_gemm_body<TAIL, OUT_BF16>(p, t, L);
+    }
   }
 #endif
 }
@@ -615,8 +678,10 @@ inline int device_cus() {
 template <class C, bool GROUPED, class TAIL = C>
 hipError_t launch(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
   const int64_t NT = (args.N + C::BN - 1) / C::BN;
-  const int64_t MT =
-      GROUPED ? (args.M + C::BM - 1) / C::BM + args.G : (args.M + C::BM - 1) / C::BM;
+  // grouped: every non-empty group adds at most one partial tile-row, and
+  // every tile-row holds at least one row
+  int64_t MT = (args.M + C::BM - 1) / C::BM;
+  if (GROUPED) MT = MT + args.G < args.M ? MT + args.G : args.M;
   const int64_t tiles = MT * NT;
   if (tiles <= 0) return hipSuccess;
   int64_t full = tiles, blocks = tiles;

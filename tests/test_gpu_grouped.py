@@ -41,6 +41,8 @@ def _run(fp8bs, qa, sa, qw, sw, offsets, out_dtype):
     ([0, 0, 300], 200, 384, torch.bfloat16),
     ([1] * 40, 128, 256, torch.float32),
     ([513, 0, 256, 257, 1], 640, 384, torch.bfloat16),
+    # last tile-rows of exactly 128 rows (half-height), 129 (full height), 44
+    ([384, 129, 300], 256, 256, torch.float32),
 ])
 def test_grouped_all_outputs(fp8bs, sizes, N, K, out):
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
@@ -123,3 +125,19 @@ def test_full_size_moe_gate_up_sampled(fp8bs):
             worst = max(worst, gu.check_gemm(ch[rows][:, nb * 128:(nb + 1) * 128], C, B,
                                               bf16=True))
     print(f"moe full-size sampled: worst err/bound = {worst:.4f}")
+
+
+def test_many_groups(fp8bs):
+    """More groups than one wave scans at a time (G = 150 > 64): the group
+    search walks several 64-group chunks; sizes 0..300 with many empty and
+    tiny groups."""
+    rng = np.random.default_rng(12)
+    sizes = rng.integers(0, 6, 150)
+    sizes[rng.choice(150, 4, replace=False)] = [300, 129, 128, 257]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, N, K = int(offsets[-1]), 128, 256
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(synth.act(M, K, case=512, tensor=0)))
+    qw, sw = _experts(len(sizes), N, K, 512)
+    c = _run(fp8bs, qa, sa, qw, sw, offsets, torch.float32)
+    C, B = oracle.block_grouped_gemm(qa, sa, qw, sw, offsets)
+    gu.check_gemm(c, C, B)
