@@ -40,11 +40,13 @@ from .e4m3 import E4M3_MAX, decode, decode_table, encode  # noqa: F401
 from .quant import (  # noqa: F401
     SCALE_FLOOR,
     quant_act_1x128,
+    quant_rows_1x128,
     quant_w_128x128,
     tile_scale,
 )
 from .gemm import (  # noqa: F401
     block_gemm,
+    block_gemm_e4m3_out,
     block_grouped_gemm,
     fused_act_gemm,
 )

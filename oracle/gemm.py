@@ -31,7 +31,7 @@ when ``|C_gpu - C| <= 2e-3 * B``.
 import numpy as np
 
 from .e4m3 import decode_table
-from .quant import TILE, quant_act_1x128
+from .quant import TILE, quant_act_1x128, quant_rows_1x128
 
 _DEC = decode_table()
 
@@ -105,3 +105,19 @@ def fused_act_gemm(x_bits, qw, sw):
     qa, sa = quant_act_1x128(x_bits)
     C, B = block_gemm(qa, sa, qw, sw)
     return qa, sa, C, B
+
+
+def block_gemm_e4m3_out(qa, sa, qw, sw):
+    """The block GEMM with its output quantized for the next FP8 GEMM.
+
+    C is computed as ``block_gemm``; its float32 rounding RN32(C) is then
+    quantized per 1x128 tile along N (``quant_rows_1x128``), the online
+    activation rule applied where the FP32 output leaves the GEMM.  A GPU
+    quantizes its own FP32 accumulator, which lies within the GEMM tolerance
+    of C rather than equal to RN32(C), so its codes are compared with these
+    exactly only where C is exact in float32, and by value bounds elsewhere.
+    Returns ``(C, B, qc, sc)``; ``sc`` float32 [N/128][M].
+    """
+    C, B = block_gemm(qa, sa, qw, sw)
+    qc, sc = quant_rows_1x128(C.astype(np.float32))
+    return C, B, qc, sc

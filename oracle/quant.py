@@ -64,11 +64,35 @@ def _quantize_group(x, r):
     return encode(y)
 
 
+def quant_rows_1x128(x):
+    """Quantize float32 values [M][K] per 1x128 tile along each row.
+
+    The steps of the online activation quantization (the pages' 1x128 tile
+    rule) applied to float32 input: this is how a GEMM's FP32 output becomes
+    the next GEMM's E4M3 input.  Returns ``(q, s)``: ``q`` uint8 [M][K];
+    ``s`` float32 [KB][M] with ``KB = ceil(K/128)``.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    KB = -(-K // TILE)
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((KB, M), dtype=np.float32)
+    for kb in range(KB):
+        k0, k1 = kb * TILE, min(K, (kb + 1) * TILE)
+        t = x[:, k0:k1]
+        amax = np.max(np.abs(t), axis=1)
+        sk, rk = tile_scale(amax)
+        q[:, k0:k1] = _quantize_group(t, rk[:, None])
+        s[kb] = sk
+    return q, s
+
+
 def quant_act_1x128(x_bits, row_chunk: int = 2048):
     """Quantize bf16 activations [M][K] per 1x128 tile.
 
-    Returns ``(q, s)``: ``q`` uint8 [M][K]; ``s`` float32 [KB][M] with
-    ``KB = ceil(K/128)``.
+    The bf16 values are widened to float32 exactly, then quantized as
+    ``quant_rows_1x128``.  Returns ``(q, s)``: ``q`` uint8 [M][K]; ``s``
+    float32 [KB][M] with ``KB = ceil(K/128)``.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     M, K = x_bits.shape
@@ -77,14 +101,7 @@ def quant_act_1x128(x_bits, row_chunk: int = 2048):
     s = np.empty((KB, M), dtype=np.float32)
     for m0 in range(0, M, row_chunk):
         m1 = min(M, m0 + row_chunk)
-        x = bf16_bits_to_f32(x_bits[m0:m1])
-        for kb in range(KB):
-            k0, k1 = kb * TILE, min(K, (kb + 1) * TILE)
-            t = x[:, k0:k1]
-            amax = np.max(np.abs(t), axis=1)
-            sk, rk = tile_scale(amax)
-            q[m0:m1, k0:k1] = _quantize_group(t, rk[:, None])
-            s[kb, m0:m1] = sk
+        q[m0:m1], s[:, m0:m1] = quant_rows_1x128(bf16_bits_to_f32(x_bits[m0:m1]))
     return q, s
 
 

@@ -208,3 +208,31 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(oquant, "_F448", np.float32(127.0))
     q, s = oracle.quant_act_1x128(np.array([[0x3F80] * 128], dtype=np.uint16))
     assert q[0, 0] != 0x7E
+
+
+def test_e4m3_out_closed_form():
+    """One-hot activation rows (448 at column k0(m), zero elsewhere) and a
+    weight on the E4M3 grid whose every 128x128 block and every column of a
+    128-row band reach 448: s_A = s_W = 1, C[m, n] = 448 * w[n, k0(m)]
+    exactly, and its 1x128 output tiles have amax 448 * 448, so the output
+    scale is exactly 448 and the output codes are the weight's own codes."""
+    rng = np.random.default_rng(9)
+    tab = oracle.decode_table()
+    # -0 is left out: the sum C = 0 + 448 * (-0) is +0, whose code differs
+    finite = tab[[c for c in range(256) if c not in (0x7F, 0xFF, 0x80)]]
+    M, N, K = 8, 384, 256
+    w = rng.choice(finite, (N, K))
+    w[::128, :] = 448.0
+    k0 = rng.integers(0, K, M)
+    a = np.zeros((M, K))
+    a[np.arange(M), k0] = 448.0
+    qa, sa = oracle.quant_act_1x128(_bf16_bits(a))
+    qw, sw = oracle.quant_w_128x128(_bf16_bits(w))
+    assert np.all(sw == 1.0)
+    C, B, qc, sc = oracle.block_gemm_e4m3_out(qa, sa, qw, sw)
+    assert np.array_equal(C, 448.0 * w[:, k0].T)
+    assert sc.shape == (N // 128, M) and np.all(sc == 448.0)
+    assert np.array_equal(qc, qw[:, k0].T)
+    # the quantized output decodes back to C within the E4M3 half-ulp bound
+    deq = oracle.decode(qc) * np.repeat(sc.T.astype(np.float64), 128, axis=1)
+    assert np.array_equal(deq, C)

@@ -200,3 +200,67 @@ def test_division_form_differs_from_reciprocal_form():
     by_r = oracle.encode(np.multiply(x, r, dtype=np.float32))
     by_s = oracle.encode(np.divide(x, s, dtype=np.float32))
     assert np.count_nonzero(by_r != by_s) > 0
+
+
+# ---- float32-input tiles (the GEMM output quantized for the next GEMM) ----
+
+def _f32_tiles(rows, k, seed):
+    """Heavy-tailed float32 values with full 24-bit significands (not bf16)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, k)) * np.exp(rng.standard_normal((rows, 1)))
+    idx = rng.choice(rows * k, max(1, rows * k // 1000), replace=False)
+    x.ravel()[idx] *= 100.0
+    x = x.astype(np.float32)
+    # most values are not bf16-representable (the widening test would be vacuous)
+    assert np.mean((x.view(np.uint32) & 0xFFFF) != 0) > 0.99
+    return x
+
+
+def test_rows_quantizer_equals_bf16_path_on_bf16_values():
+    bits = _heavy_tiles(64, 512, seed=20)
+    qa, sa = oracle.quant_act_1x128(bits)
+    qr, sr = oracle.quant_rows_1x128(_f32(bits))
+    assert np.array_equal(qa, qr) and np.array_equal(sa, sr)
+
+
+def test_rows_quantizer_argmax_scale_and_round_trip():
+    x = _f32_tiles(256, 1024, seed=21)
+    q, s = oracle.quant_rows_1x128(x)
+    xt = x.reshape(256, 8, 128)
+    amax = np.max(np.abs(xt), axis=2)
+    # scale: amax / 448 correctly rounded in float32
+    assert np.array_equal(s.T, np.divide(amax, np.float32(448.0), dtype=np.float32))
+    assert np.all(np.abs(s.T.astype(np.float64) * 448.0 - amax) <= amax * 2.0 ** -24)
+    top = np.take_along_axis(q.reshape(256, 8, 128), np.argmax(np.abs(xt), axis=2)[..., None],
+                             axis=2)[..., 0]
+    assert np.all((top & 0x7F) == 0x7E)
+    deq = oracle.decode(q) * np.repeat(s.T.astype(np.float64), 128, axis=1)
+    bound = np.maximum(np.abs(x) / 16.0, np.repeat(amax, 128, axis=1) / 458752.0) * (1 + 2.0 ** -20)
+    ratio = np.abs(x.astype(np.float64) - deq) / bound
+    assert ratio.max() <= 1.0 and ratio.max() > 0.9
+
+
+def test_rows_quantizer_top_code_for_random_float32_maxima():
+    # the scale rule maps any float32 maximum (not only bf16 ones) to 448
+    rng = np.random.default_rng(22)
+    a = np.exp2(rng.uniform(-60, 100, 200000)).astype(np.float32)
+    s, r = oracle.tile_scale(a)
+    y = np.multiply(a, r, dtype=np.float32)
+    assert np.all(np.abs(y.astype(np.float64) - 448.0) <= 448.0 * 2.0 ** -22)
+    assert np.all(oracle.encode(y) == 0x7E)
+
+
+def test_rows_quantizer_matches_argmin_encoder():
+    x = _f32_tiles(4, 256, seed=23)
+    q, s = oracle.quant_rows_1x128(x)
+    tab = oracle.decode_table()
+    for m in range(4):
+        for kb in range(2):
+            t = x[m, kb * 128:(kb + 1) * 128]
+            a = max(float(np.max(np.abs(t))), 2.0 ** -64)
+            r = np.float32(np.float32(448.0) / np.float32(a))
+            for j in range(128):
+                y = float(np.float32(t[j] * r))
+                mag = min(abs(y), 448.0)
+                best = min(range(0x7F), key=lambda c: (abs(tab[c] - mag), c % 2))
+                assert q[m, kb * 128 + j] == best | (0x80 if math.copysign(1.0, y) < 0 else 0)
