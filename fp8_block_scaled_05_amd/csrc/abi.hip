@@ -53,21 +53,30 @@ int fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, ui
       fp8bs::launch_quant_w(w, N, K, ldw, q, ldq, s, static_cast<hipStream_t>(stream)));
 }
 
-int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa, int64_t ldsa,
-                   const uint8_t* b, int64_t ldb, const float* sb, void* c, int64_t ldc,
-                   int out_kind, int64_t M, int64_t N, int64_t K, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the dense entry points.  out: element type of c; for E4M3
+// output, sc/ldsc receive the per-1x128 output scales.
+int block_gemm_impl(int a_kind, const void* a, int64_t lda, float* sa, int64_t ldsa,
+                    const uint8_t* b, int64_t ldb, const float* sb, void* c, int64_t ldc,
+                    fp8bs::OutKind out, float* sc, int64_t ldsc, int64_t M, int64_t N,
+                    int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   if (a_kind != FP8BS_A_E4M3 && a_kind != FP8BS_A_BF16) return FP8BS_ERR_DTYPE;
-  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
   if (M < 0 || N < 0 || K <= 0 || K % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (out == fp8bs::kOutE4M3 && N % kTile != 0) return FP8BS_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BS_OK;
   if (!a || !b || !sb || !c) return FP8BS_ERR_NULL;
   if (a_kind == FP8BS_A_E4M3 && !sa) return FP8BS_ERR_NULL;
+  if (out == fp8bs::kOutE4M3 && !sc) return FP8BS_ERR_NULL;
   if (!ld_ok(lda, K) || !ld_ok(ldb, K) || ldc < N) return FP8BS_ERR_LAYOUT;
   if (sa && ldsa < M) return FP8BS_ERR_LAYOUT;
-  const uintptr_t c_align = out_kind == FP8BS_OUT_F32 ? 4 : 2;
+  const uintptr_t c_align = out == fp8bs::kOutF32 ? 4 : out == fp8bs::kOutBF16 ? 2 : 16;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sb, 4) ||
       (sa && !aligned(sa, 4)))
+    return FP8BS_ERR_LAYOUT;
+  if (out == fp8bs::kOutE4M3 && (!ld_ok(ldc, N) || ldsc < M || !aligned(sc, 4)))
     return FP8BS_ERR_LAYOUT;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -77,6 +86,8 @@ int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa, int64_t ld
   g.sb = sb;
   g.c = c;
   g.ldc = ldc;
+  g.sc = sc;
+  g.ldsc = ldsc;
   g.M = M;
   g.N = N;
   g.K = K;
@@ -101,26 +112,28 @@ int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa, int64_t ld
     g.sa = ws;
     g.ldsa = wlds;
   }
-  return hip_status(fp8bs::launch_block_gemm(g, out_kind == FP8BS_OUT_BF16, st));
+  return hip_status(fp8bs::launch_block_gemm(g, out, st));
 }
 
-int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
-                           const uint8_t* b, int64_t ldb, int64_t b_group_stride,
-                           const float* sb, void* c, int64_t ldc, int out_kind,
-                           const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N,
-                           int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+// Shared body of the grouped entry points.
+int grouped_gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                      const uint8_t* b, int64_t ldb, int64_t b_group_stride, const float* sb,
+                      void* c, int64_t ldc, fp8bs::OutKind out, float* sc, int64_t ldsc,
+                      const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N,
+                      int64_t K, void* stream) {
   if (G < 1 || G > kMaxGroups || M_total < 0 || N < 0 || K <= 0 || K % kTile != 0)
     return FP8BS_ERR_SHAPE;
+  if (out == fp8bs::kOutE4M3 && N % kTile != 0) return FP8BS_ERR_SHAPE;
   if (M_total == 0 || N == 0) return FP8BS_OK;
   if (!a || !sa || !b || !sb || !c || !group_offsets) return FP8BS_ERR_NULL;
+  if (out == fp8bs::kOutE4M3 && !sc) return FP8BS_ERR_NULL;
   if (!ld_ok(lda, K) || !ld_ok(ldb, K) || ldc < N || ldsa < M_total) return FP8BS_ERR_LAYOUT;
   if (b_group_stride % 16 != 0 || b_group_stride < (N - 1) * ldb + K) return FP8BS_ERR_LAYOUT;
-  const uintptr_t c_align = out_kind == FP8BS_OUT_F32 ? 4 : 2;
+  const uintptr_t c_align = out == fp8bs::kOutF32 ? 4 : out == fp8bs::kOutBF16 ? 2 : 16;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sa, 4) ||
       !aligned(sb, 4) || !aligned(group_offsets, 4))
+    return FP8BS_ERR_LAYOUT;
+  if (out == fp8bs::kOutE4M3 && (!ld_ok(ldc, N) || ldsc < M_total || !aligned(sc, 4)))
     return FP8BS_ERR_LAYOUT;
   fp8bs::GemmArgs g{};
   g.a = a;
@@ -133,14 +146,66 @@ int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64
   g.sb = sb;
   g.c = c;
   g.ldc = ldc;
+  g.sc = sc;
+  g.ldsc = ldsc;
   g.M = M_total;
   g.N = N;
   g.K = K;
   g.sb_ld = K / kTile;
   g.group_offsets = group_offsets;
   g.G = G;
-  return hip_status(fp8bs::launch_grouped_gemm(g, out_kind == FP8BS_OUT_BF16,
-                                               static_cast<hipStream_t>(stream)));
+  return hip_status(fp8bs::launch_grouped_gemm(g, out, static_cast<hipStream_t>(stream)));
+}
+
+fp8bs::OutKind out_of(int out_kind) {
+  return out_kind == FP8BS_OUT_BF16 ? fp8bs::kOutBF16 : fp8bs::kOutF32;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa, int64_t ldsa,
+                   const uint8_t* b, int64_t ldb, const float* sb, void* c, int64_t ldc,
+                   int out_kind, int64_t M, int64_t N, int64_t K, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+  return block_gemm_impl(a_kind, a, lda, sa, ldsa, b, ldb, sb, c, ldc, out_of(out_kind),
+                         nullptr, 0, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int fp8_block_gemm_e4m3_out(int a_kind, const void* a, int64_t lda, float* sa, int64_t ldsa,
+                            const uint8_t* b, int64_t ldb, const float* sb, uint8_t* qc,
+                            int64_t ldqc, float* sc, int64_t ldsc, int64_t M, int64_t N,
+                            int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  return block_gemm_impl(a_kind, a, lda, sa, ldsa, b, ldb, sb, qc, ldqc, fp8bs::kOutE4M3, sc,
+                         ldsc, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                           const uint8_t* b, int64_t ldb, int64_t b_group_stride,
+                           const float* sb, void* c, int64_t ldc, int out_kind,
+                           const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N,
+                           int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+  return grouped_gemm_impl(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, c, ldc,
+                           out_of(out_kind), nullptr, 0, group_offsets, G, M_total, N, K,
+                           stream);
+}
+
+int fp8_block_grouped_gemm_e4m3_out(const uint8_t* a, int64_t lda, const float* sa,
+                                    int64_t ldsa, const uint8_t* b, int64_t ldb,
+                                    int64_t b_group_stride, const float* sb, uint8_t* qc,
+                                    int64_t ldqc, float* sc, int64_t ldsc,
+                                    const int32_t* group_offsets, int64_t G, int64_t M_total,
+                                    int64_t N, int64_t K, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return grouped_gemm_impl(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, qc, ldqc,
+                           fp8bs::kOutE4M3, sc, ldsc, group_offsets, G, M_total, N, K, stream);
 }
 
 size_t fp8bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t G) {

@@ -12,6 +12,8 @@
 // - few rows (decode-like, weight-bandwidth bound): short tiles so that the
 //   weight matrix is spread over many workgroups and every weight byte is
 //   read once; 1 wave along M; four LDS stages (three K groups in flight).
+//   E4M3 output (quantized per 128 output columns) needs tiles of whole
+//   128-column groups, so it takes the 64x128 tile for every M <= 64.
 
 #include "gemm_kernel.hpp"
 
@@ -27,14 +29,16 @@ using Rows32Cfg = gemm::Cfg<32, 32, 1, 2, 4, 1>;
 using Rows64Cfg = gemm::Cfg<64, 128, 1, 4, 4, 1>;
 }  // namespace
 
-hipError_t launch_block_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
-  if (args.M <= 32) return gemm::launch<Rows32Cfg, false>(args, out_bf16, stream);
-  if (args.M <= 64) return gemm::launch<Rows64Cfg, false>(args, out_bf16, stream);
-  return gemm::launch<LargeCfg, false, LargeTail>(args, out_bf16, stream);
+hipError_t launch_block_gemm(const GemmArgs& args, OutKind out, hipStream_t stream) {
+  // E4M3 output quantizes whole 128-column tiles inside a workgroup: the
+  // 32-column few-row tile cannot, so E4M3 output uses the 64x128 tile
+  if (args.M <= 32 && out != kOutE4M3) return gemm::launch<Rows32Cfg, false>(args, out, stream);
+  if (args.M <= 64) return gemm::launch<Rows64Cfg, false>(args, out, stream);
+  return gemm::launch<LargeCfg, false, LargeTail>(args, out, stream);
 }
 
-hipError_t launch_grouped_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
-  return gemm::launch<LargeCfg, true, LargeTail>(args, out_bf16, stream);
+hipError_t launch_grouped_gemm(const GemmArgs& args, OutKind out, hipStream_t stream) {
+  return gemm::launch<LargeCfg, true, LargeTail>(args, out, stream);
 }
 
 }  // namespace fp8bs

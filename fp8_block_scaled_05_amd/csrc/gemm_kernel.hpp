@@ -213,7 +213,13 @@ __device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t
       const int rr = r < rows_a ? r : rows_a - 1;
       lp.tile[j] = (uint32_t)rr * (uint32_t)p.lda + chunk * 16;
     } else {
-      const int rr = (r - C::BM) < rows_b ? (r - C::BM) : rows_b - 1;
+      // B rows are staged permuted within each wave's TN columns: LDS row
+      // 16 f + l of a wave's block holds tile column FN l + f, so the lane
+      // that produces MFMA column l of fragment f holds, over f, FN
+      // consecutive output columns (one vector store per output row)
+      const int rb = r - C::BM, wb = rb / C::TN, rw = rb % C::TN;
+      const int col = wb * C::TN + C::FN * (rw % 16) + rw / 16;
+      const int rr = col < rows_b ? col : rows_b - 1;
       lp.tile[j] = (uint32_t)rr * (uint32_t)p.ldb + chunk * 16;
     }
   }
@@ -454,9 +460,140 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
 struct LdsSet {
   uint8_t* st[4];
   float* sc[4];
+  float* red;  // E4M3 output: per-wave row maxima [WN][BM]
+  float* rcp;  // E4M3 output: per-row reciprocals [BN/128][BM]
 };
 
-template <class C, bool OUT_BF16>
+template <class T, int N>
+struct Vec {
+  typedef T type __attribute__((ext_vector_type(N)));
+};
+
+// fp32 or bf16 output.  Lane (g, l) holds rows 16 i + 4 g + r of the wave's
+// sub-tile and, through the permuted B staging, the FN consecutive columns
+// FN l .. FN l + FN - 1 of the wave's TN columns: one store per row (vector
+// when the row start is aligned for it).
+template <class C, int OUT>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoords& t,
+                                           const v4f (&acc)[C::FM][C::FN], int wm, int wn,
+                                           int lane) {
+  using T = typename std::conditional<OUT == kOutBF16, uint16_t, float>::type;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int64_t col = t.col0 + wn * C::TN + C::FN * l16;
+  const bool vec = C::FN > 1 && reinterpret_cast<uintptr_t>(p.c) % (C::FN * sizeof(T)) == 0 &&
+                   p.ldc % C::FN == 0;
+  T* const out = reinterpret_cast<T*>(p.c);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = t.row0 + wm * C::TM + 16 * i + 4 * g4 + r;
+      if (row >= t.row_end) continue;
+      T v[C::FN];
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (OUT == kOutBF16) {
+          v[j] = f32_to_bf16_rne(acc[i][j][r]);
+        } else {
+          v[j] = acc[i][j][r];
+        }
+      }
+      T* const dst = out + row * p.ldc + col;
+      if constexpr (C::FN > 1) {
+        if (vec && col + C::FN <= p.N) {
+          typename Vec<T, C::FN>::type w;
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) w[j] = v[j];
+          *reinterpret_cast<typename Vec<T, C::FN>::type*>(dst) = w;
+          continue;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        if (col + j < p.N) dst[j] = v[j];
+    }
+  }
+}
+
+// E4M3 output quantized per 1x128 tile along N, the next layer's FP8 input
+// (pages: "How online quantization in DeepSeek-V3 differs from delayed
+// quantization", item 1, and "How the unified E4M3 format adds to
+// DeepSeek-V3's efficiency", section "Fine-grained quantization strategy":
+// the same online 1x128 activation quantization, applied to the FP32 output
+// before it leaves the kernel).  A row's 128-column tile spans 128 / TN
+// waves: each wave reduces its TN columns (lanes, then the 16 lanes of a
+// DPP row), the partial maxima meet in LDS, one thread per (row, tile)
+// forms the scale and reciprocal exactly as the activation quantizer does,
+// and each lane converts and stores its FN consecutive codes per row.
+// Requires BN % 128 == 0 and N % 128 == 0 (whole tiles).
+template <class C>
+__device__ __forceinline__ void store_tile_e4m3(const GemmArgs& p, const TileCoords& t,
+                                                const v4f (&acc)[C::FM][C::FN], int wm,
+                                                int wn, int lane, float* red, float* rcp) {
+  static_assert(C::BN % 128 == 0, "E4M3 output needs whole 128-column tiles per workgroup");
+  constexpr int WPB = 128 / C::TN;  // waves across one 128-column tile
+  constexpr int NBT = C::BN / 128;  // 128-column tiles per workgroup tile
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) m = fmaxf(m, fabsf(acc[i][j][r]));
+      m = max_row16(m);
+      if (l16 == 0) red[wn * C::BM + wm * C::TM + 16 * i + 4 * g4 + r] = m;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < NBT * C::BM; idx += C::THREADS) {
+    const int nb = idx / C::BM, rt = idx % C::BM;
+    float amax = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) amax = fmaxf(amax, red[(nb * WPB + w) * C::BM + rt]);
+    float s, rr;
+    group_scale(amax, s, rr);
+    rcp[idx] = rr;
+    const int64_t row = t.row0 + rt, cb = t.col0 / 128 + nb;
+    if (row < t.row_end && cb * 128 < p.N) p.sc[cb * p.ldsc + row] = s;
+  }
+  __syncthreads();
+  const int64_t col = t.col0 + wn * C::TN + C::FN * l16;
+  if (col >= p.N) return;  // the wave's whole 128-column tile is past N
+  const int nbw = (wn * C::TN) / 128;
+  uint8_t* const out = reinterpret_cast<uint8_t*>(p.c);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const float4 r4 =
+        *reinterpret_cast<const float4*>(rcp + nbw * C::BM + wm * C::TM + 16 * i + 4 * g4);
+    const float rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = t.row0 + wm * C::TM + 16 * i + 4 * g4 + r;
+      if (row >= t.row_end) continue;
+      uint8_t* const dst = out + row * p.ldc + col;
+      float y[C::FN];
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) y[j] = acc[i][j][r] * rv[r];
+      if constexpr (C::FN == 1) {
+        *dst = (uint8_t)cvt2_e4m3<false>(y[0], 0.f, 0u);
+      } else if constexpr (C::FN == 2) {
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)cvt2_e4m3<false>(y[0], y[1], 0u);
+      } else {
+        static_assert(C::FN % 4 == 0, "FN of 1, 2 or a multiple of 4");
+        typename Vec<uint32_t, C::FN / 4>::type w;
+#pragma unroll
+        for (int q = 0; q < C::FN / 4; ++q) {
+          const uint32_t lo = cvt2_e4m3<false>(y[4 * q], y[4 * q + 1], 0u);
+          w[q] = cvt2_e4m3<true>(y[4 * q + 2], y[4 * q + 3], lo);
+        }
+        *reinterpret_cast<typename Vec<uint32_t, C::FN / 4>::type*>(dst) = w;
+      }
+    }
+  }
+}
+
+template <class C, int OUT>
 __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoords& t,
                                                 const LdsSet& L) {
   // wave index in an SGPR so that per-wave values stay scalar
@@ -580,26 +717,10 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
     }
   }
 
-  // Epilogue: a lane holds rows 4*(lane/16) + r, column lane%16 of each
-  // 16x16 tile.
-  const int g4 = lane >> 4, l16 = lane & 15;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int64_t col = t.col0 + wn * C::TN + 16 * j + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = t.row0 + wm * C::TM + 16 * i + 4 * g4 + r;
-        if (row < t.row_end && col < p.N) {
-          if constexpr (OUT_BF16) {
-            reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
-          } else {
-            reinterpret_cast<float*>(p.c)[row * p.ldc + col] = acc[i][j][r];
-          }
-        }
-      }
-    }
+  if constexpr (OUT == kOutE4M3) {
+    store_tile_e4m3<C>(p, t, acc, wm, wn, lane, L.red, L.rcp);
+  } else {
+    store_tile<C, OUT>(p, t, acc, wm, wn, lane);
   }
 }
 
@@ -614,7 +735,7 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
 // rows.  TAIL == C: no half tiles.
 // The buffer-resource type exists only for the device; the host pass sees an
 // empty kernel (it only needs the launch stub).
-template <class C, class TAIL, bool GROUPED, bool OUT_BF16>
+template <class C, class TAIL, bool GROUPED, int OUT>
 __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int64_t full) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(TAIL::THREADS == C::THREADS && TAIL::BN == C::BN && 2 * TAIL::BM == C::BM ||
@@ -631,7 +752,10 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
   __shared__ __attribute__((aligned(16))) float sc1[SF];
   __shared__ __attribute__((aligned(16))) float sc2[NS > 2 ? SF : 4];
   __shared__ __attribute__((aligned(16))) float sc3[NS > 3 ? SF : 4];
-  const LdsSet L{{st0, st1, st2, st3}, {sc0, sc1, sc2, sc3}};
+  constexpr bool Q = OUT == kOutE4M3;
+  __shared__ __attribute__((aligned(16))) float red[Q ? C::WN * C::BM : 4];
+  __shared__ __attribute__((aligned(16))) float rcp[Q ? C::BN / 128 * C::BM : 4];
+  const LdsSet L{{st0, st1, st2, st3}, {sc0, sc1, sc2, sc3}, red, rcp};
   const int64_t bid = blockIdx.x;
   TileCoords t;
   if constexpr (GROUPED) {
@@ -642,21 +766,21 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
     grouped_tile<C>(p, xcd_remap(bid, T), MT, t);
     if constexpr (HALVES) {
       if (t.row_end - t.row0 <= TAIL::BM) {
-        block_gemm_body<TAIL, OUT_BF16>(p, t, L);
+        block_gemm_body<TAIL, OUT>(p, t, L);
         return;
       }
     }
-    block_gemm_body<C, OUT_BF16>(p, t, L);
+    block_gemm_body<C, OUT>(p, t, L);
   } else {
     if (bid < full) {
       dense_tile<C>(p, xcd_remap(bid, full), t);
-      block_gemm_body<C, OUT_BF16>(p, t, L);
+      block_gemm_body<C, OUT>(p, t, L);
     } else if constexpr (HALVES) {
       const int64_t j = xcd_remap(bid - full, (int64_t)gridDim.x - full);
       dense_tile<C>(p, full + j / 2, t);
       t.row0 += (j & 1) * TAIL::BM;
       if (t.row0 >= t.row_end) return;  // lower half below the last row
-      block_gemm_body<TAIL, OUT_BF16>(p, t, L);
+      block_gemm_body<TAIL, OUT>(p, t, L);
     }
   }
 #endif
@@ -676,7 +800,7 @@ inline int device_cus() {
 }
 
 template <class C, bool GROUPED, class TAIL = C>
-hipError_t launch(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
+hipError_t launch(const GemmArgs& args, OutKind out, hipStream_t stream) {
   const int64_t NT = (args.N + C::BN - 1) / C::BN;
   // grouped: every non-empty group adds at most one partial tile-row, and
   // every tile-row holds at least one row
@@ -693,12 +817,24 @@ hipError_t launch(const GemmArgs& args, bool out_bf16, hipStream_t stream) {
     }
   }
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (out_bf16) {
-    hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, true>), dim3((unsigned)blocks),
-                       dim3(C::THREADS), 0, stream, args, full);
-  } else {
-    hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, false>), dim3((unsigned)blocks),
-                       dim3(C::THREADS), 0, stream, args, full);
+  const dim3 grid((unsigned)blocks), block(C::THREADS);
+  switch (out) {
+    case kOutF32:
+      hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, kOutF32>), grid, block, 0, stream,
+                         args, full);
+      break;
+    case kOutBF16:
+      hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, kOutBF16>), grid, block, 0, stream,
+                         args, full);
+      break;
+    default:
+      if constexpr (C::BN % 128 == 0) {
+        hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, kOutE4M3>), grid, block, 0,
+                           stream, args, full);
+      } else {
+        return hipErrorInvalidConfiguration;  // E4M3 output needs whole 128-column tiles
+      }
+      break;
   }
   return hipGetLastError();
 }

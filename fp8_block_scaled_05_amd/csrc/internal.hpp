@@ -16,8 +16,10 @@ struct GemmArgs {
   int64_t b_group_stride;  // bytes between experts' weights (grouped only)
   const float* sb;
   int64_t sb_ld;  // floats between consecutive 128-row bands of S_W (= K/128 of the whole GEMM)
-  void* c;
+  void* c;       // output: fp32, bf16 or E4M3 codes [M][ldc]
   int64_t ldc;
+  float* sc;     // E4M3 output only: scale of row m, 128-column block nb at sc[nb*ldsc + m]
+  int64_t ldsc;
   int64_t M;  // rows (dense) or M_total (grouped)
   int64_t N;
   int64_t K;
@@ -32,8 +34,11 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                           uint8_t* q, int64_t ldq, float* s, hipStream_t stream);
 
-hipError_t launch_block_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream);
+// Output element type of the GEMM kernels.
+enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2 };
 
-hipError_t launch_grouped_gemm(const GemmArgs& args, bool out_bf16, hipStream_t stream);
+hipError_t launch_block_gemm(const GemmArgs& args, OutKind out, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const GemmArgs& args, OutKind out, hipStream_t stream);
 
 }  // namespace fp8bs

@@ -24,6 +24,8 @@ EXPORTS = (
     "fp8_quant_w_128x128",
     "fp8_block_gemm",
     "fp8_block_grouped_gemm",
+    "fp8_block_gemm_e4m3_out",
+    "fp8_block_grouped_gemm_e4m3_out",
     "fp8bs_workspace_bytes",
     "fp8bs_status_string",
     "fp8bs_last_hip_error",
@@ -41,6 +43,10 @@ _SIGNATURES = {
                         _i64, _i64, _i64, _p, _sz, _p], _int),
     "fp8_block_grouped_gemm": ([_p, _i64, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _int,
                                 _p, _i64, _i64, _i64, _i64, _p, _sz, _p], _int),
+    "fp8_block_gemm_e4m3_out": ([_int, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64,
+                                 _i64, _i64, _i64, _p, _sz, _p], _int),
+    "fp8_block_grouped_gemm_e4m3_out": ([_p, _i64, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _p,
+                                         _i64, _p, _i64, _i64, _i64, _i64, _p, _sz, _p], _int),
     "fp8bs_workspace_bytes": ([_int, _i64, _i64, _i64, _i64], _sz),
     "fp8bs_status_string": ([_int], ctypes.c_char_p),
     "fp8bs_last_hip_error": ([], _int),
@@ -195,3 +201,59 @@ def fp8_block_grouped_gemm(a, sa, b, sb, group_offsets, out=None, out_dtype=torc
                                       _out_kind(out.dtype), _ptr(group_offsets), G, M_total, N,
                                       K, None, 0, _stream(a)), "fp8_block_grouped_gemm")
     return out
+
+
+def _e4m3_outputs(M, N, qc, sc, device):
+    if qc is None:
+        qc = torch.empty(M, N, dtype=torch.uint8, device=device)
+    if sc is None:
+        sc = torch.empty(N // 128, M, dtype=torch.float32, device=device)
+    if qc.dtype != torch.uint8 or sc.dtype != torch.float32 or sc.dim() != 2:
+        raise ValueError("qc must be uint8 [M][ldqc], sc float32 [N/128][ldsc]")
+    return qc, sc
+
+
+def fp8_block_gemm_e4m3_out(a, sa, b, sb, qc=None, sc=None, workspace=None):
+    """As ``fp8_block_gemm``, with C quantized per 1x128 tile along N.
+
+    Returns ``(qc, sc)``: E4M3 codes uint8 [M][N] and scales fp32
+    [N/128][ldsc] (``sc[nb, m]``), the layout ``fp8_block_gemm`` takes as
+    its activation input.
+    """
+    _need_device(a, sa, b, sb, qc, sc, workspace)
+    a_kind = A_E4M3 if a.dtype == torch.uint8 else A_BF16 if a.dtype == torch.bfloat16 else None
+    if a_kind is None:
+        raise ValueError("a must be uint8 (E4M3 codes) or bfloat16")
+    M, K = a.shape
+    N = b.shape[0]
+    qc, sc = _e4m3_outputs(M, N, qc, sc, a.device)
+    ws_need = workspace_bytes(OP_GEMM_BF16, M, N, K) if a_kind == A_BF16 else 0
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ldsa = sa.shape[1] if sa is not None else 0
+    _check(lib.fp8_block_gemm_e4m3_out(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
+                                       _ptr(sb), _ptr(qc), _ld(qc), _ptr(sc), sc.shape[1], M, N,
+                                       K, _ptr(workspace), ws_bytes, _stream(a)),
+           "fp8_block_gemm_e4m3_out")
+    return qc, sc
+
+
+def fp8_block_grouped_gemm_e4m3_out(a, sa, b, sb, group_offsets, qc=None, sc=None):
+    """As ``fp8_block_grouped_gemm``, with C quantized per 1x128 tile along N.
+
+    Returns ``(qc, sc)`` as ``fp8_block_gemm_e4m3_out``.
+    """
+    _need_device(a, sa, b, sb, group_offsets, qc, sc)
+    if group_offsets.dtype != torch.int32:
+        raise ValueError("group_offsets must be int32")
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    qc, sc = _e4m3_outputs(M_total, N, qc, sc, a.device)
+    _check(lib.fp8_block_grouped_gemm_e4m3_out(_ptr(a), _ld(a), _ptr(sa), sa.shape[1], _ptr(b),
+                                               b.stride(1), b.stride(0), _ptr(sb), _ptr(qc),
+                                               _ld(qc), _ptr(sc), sc.shape[1],
+                                               _ptr(group_offsets), G, M_total, N, K, None, 0,
+                                               _stream(a)),
+           "fp8_block_grouped_gemm_e4m3_out")
+    return qc, sc

@@ -141,6 +141,33 @@ int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa,
                    size_t workspace_bytes, void* stream);
 
 /*
+ * fp8_block_gemm with the output quantized for the next FP8 GEMM: C is
+ * computed exactly as by fp8_block_gemm (FP32 accumulator) and then
+ * quantized per 1x128 tile along N by the online rule above, inside the
+ * GEMM, so that (qc, sc) can be passed on as the E4M3 activation (a, sa) of
+ * a following GEMM with K' = N.
+ * Pages: "Advantages of using FP8 for GEMM operations in DeepSeek-V3",
+ * items 1 and 8 (FP8 GEMMs throughout the layers); "How online quantization
+ * in DeepSeek-V3 differs from delayed quantization", item 1 (activations
+ * quantized per 1x128 tile from their current values); "How the unified
+ * E4M3 format adds to DeepSeek-V3's efficiency", section "Fine-grained
+ * quantization strategy".
+ *
+ *   a, sa, b, sb, workspace  as fp8_block_gemm.
+ *   qc   [out] E4M3 codes [M][ldqc]; ldqc >= N, a multiple of 16; 16-byte
+ *              aligned.
+ *   sc   [out] fp32 scales: sc(m, nb) at sc[nb*ldsc + m] for
+ *              nb = 0..N/128-1, ldsc >= M (the layout of sa).
+ * Errors: as fp8_block_gemm; N not a multiple of 128 -> ERR_SHAPE; sc NULL
+ *         -> ERR_NULL; ldsc < M -> ERR_LAYOUT.
+ */
+int fp8_block_gemm_e4m3_out(int a_kind, const void* a, int64_t lda, float* sa,
+                            int64_t ldsa, const uint8_t* b, int64_t ldb,
+                            const float* sb, uint8_t* qc, int64_t ldqc,
+                            float* sc, int64_t ldsc, int64_t M, int64_t N,
+                            int64_t K, void* workspace,
+                            size_t workspace_bytes, void* stream);
+/*
  * Grouped (MoE) block-scaled FP8 GEMM: rows group_offsets[g] ..
  * group_offsets[g+1]-1 of A are multiplied by expert g's weight.
  * Pages: "Advantages of using FP8 for GEMM operations in DeepSeek-V3",
@@ -167,6 +194,23 @@ int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * fp8_block_grouped_gemm with E4M3 output quantized per 1x128 tile along N,
+ * as fp8_block_gemm_e4m3_out (same pages).  qc [M_total][ldqc] codes and
+ * sc(m, nb) at sc[nb*ldsc + m], ldsc >= M_total; every row 0..M_total-1
+ * gets its codes and scales.
+ * Errors: as fp8_block_grouped_gemm; N not a multiple of 128 -> ERR_SHAPE;
+ *         sc NULL -> ERR_NULL; ldsc < M_total -> ERR_LAYOUT.
+ */
+int fp8_block_grouped_gemm_e4m3_out(const uint8_t* a, int64_t lda,
+                                    const float* sa, int64_t ldsa,
+                                    const uint8_t* b, int64_t ldb,
+                                    int64_t b_group_stride, const float* sb,
+                                    uint8_t* qc, int64_t ldqc, float* sc,
+                                    int64_t ldsc, const int32_t* group_offsets,
+                                    int64_t G, int64_t M_total, int64_t N,
+                                    int64_t K, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 /* Workspace bytes an entry point needs for the given sizes (0 if none). */
 size_t fp8bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
                              int64_t G);

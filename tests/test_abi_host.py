@@ -138,6 +138,42 @@ def test_grouped_validation(fp8bs):
     assert g(out_kind=3) == fp8bs.ERR_DTYPE
 
 
+def test_e4m3_out_validation(fp8bs):
+    lib = fp8bs.lib
+
+    def d(a_kind=0, a=P, lda=256, sa=P, ldsa=64, b=P, ldb=256, sb=P, qc=P, ldqc=256, sc=P,
+          ldsc=64, M=64, N=256, K=256, ws=0, ws_bytes=0):
+        return lib.fp8_block_gemm_e4m3_out(a_kind, a, lda, sa, ldsa, b, ldb, sb, qc, ldqc, sc,
+                                           ldsc, M, N, K, ws, ws_bytes, None)
+
+    assert d(a_kind=3) == fp8bs.ERR_DTYPE
+    assert d(N=200) == fp8bs.ERR_SHAPE  # the output tiles are whole 128-column groups
+    assert d(K=130) == fp8bs.ERR_SHAPE
+    assert d(M=0, a=0, b=0, qc=0, sc=0) == fp8bs.OK
+    assert d(sc=0) == fp8bs.ERR_NULL
+    assert d(qc=0) == fp8bs.ERR_NULL
+    assert d(ldsc=63) == fp8bs.ERR_LAYOUT
+    assert d(ldqc=264 - 1) == fp8bs.ERR_LAYOUT
+    assert d(ldqc=128) == fp8bs.ERR_LAYOUT
+    assert d(qc=P + 4) == fp8bs.ERR_LAYOUT
+    assert d(sc=P + 2) == fp8bs.ERR_LAYOUT
+    assert d(a_kind=1, sa=0) == fp8bs.ERR_WORKSPACE
+
+    def g(a=P, lda=256, sa=P, ldsa=64, b=P, ldb=256, bstride=256 * 256, sb=P, qc=P, ldqc=256,
+          sc=P, ldsc=64, off=P, G=4, M=64, N=256, K=256):
+        return lib.fp8_block_grouped_gemm_e4m3_out(a, lda, sa, ldsa, b, ldb, bstride, sb, qc,
+                                                   ldqc, sc, ldsc, off, G, M, N, K, None, 0,
+                                                   None)
+
+    assert g(N=384 - 64) == fp8bs.ERR_SHAPE
+    assert g(G=0) == fp8bs.ERR_SHAPE
+    assert g(M=0) == fp8bs.OK
+    assert g(sc=0) == fp8bs.ERR_NULL
+    assert g(off=0) == fp8bs.ERR_NULL
+    assert g(ldsc=10) == fp8bs.ERR_LAYOUT
+    assert g(qc=P + 8) == fp8bs.ERR_LAYOUT
+
+
 def test_workspace_query(fp8bs):
     lib = fp8bs.lib
     assert lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_E4M3, 64, 128, 256, 0) == 0
