@@ -10,9 +10,11 @@ with all inputs resident in HBM.
 The same run also times, outside the timed steps, the other workloads of the
 path: the activation and weight quantizers alone at 8192x7168 / 18432x7168
 (GB/s, buffers rotated past the 256 MB Infinity Cache), the grouped MoE GEMM
-(32 experts, top-8 of 4096 tokens, gate/up and down) and the skinny GEMM with
-in-call activation quantization (M = 16, 64), and the CPU oracle on a bounded
-sample of the dense step (``cpu_baseline``).
+(32 experts, top-8 of 4096 tokens, gate/up and down), the skinny GEMM with
+in-call activation quantization (M = 16, 64), the dense GEMM with its output
+quantized for the next FP8 GEMM (against bf16 output followed by the
+activation quantizer), and the CPU oracle on a bounded sample of the dense
+step (``cpu_baseline``).
 
 The default 300 warm-up steps (about 0.2 s) bring the engine clock to its
 sustained level before the timed steps; with only a few warm-up steps the
@@ -113,9 +115,31 @@ def _dense_setup(torch, fp8bs, synth):
     return a, w, qa, sa, qw, sw, c
 
 
-def _parts(torch, fp8bs, synth, iters=30):
+def _parts(torch, fp8bs, synth, dense, iters=30):
     out = {}
     tm = Timer(torch)
+
+    # the dense GEMM with its output quantized for the next FP8 GEMM (E4M3
+    # codes + 1x128 scales written by the GEMM), timed interleaved with the
+    # unfused route: bf16 output, then the activation quantizer on it
+    qa, sa, qw, sw = dense
+    qc = torch.empty(M, N, dtype=torch.uint8, device="cuda")
+    scq = torch.empty(N // 128, M, dtype=torch.float32, device="cuda")
+    cb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    qc2 = torch.empty(M, N, dtype=torch.uint8, device="cuda")
+    sc2 = torch.empty(N // 128, M, dtype=torch.float32, device="cuda")
+    for i in range(iters + 5):
+        f = lambda: fp8bs.fp8_block_gemm_e4m3_out(qa, sa, qw, sw, qc=qc, sc=scq)
+        (tm.run("gemm_q", f) if i >= 5 else f())
+        f2 = lambda: (fp8bs.fp8_block_gemm(qa, sa, qw, sw, out=cb),
+                      fp8bs.fp8_quant_act_1x128(cb, qc2, sc2))
+        (tm.run("gemm_then_q", f2) if i >= 5 else f2())
+    ms, ms2 = tm.avg_ms("gemm_q"), tm.avg_ms("gemm_then_q")
+    out["dense_gemm_e4m3_out_M4096_N18432_K7168"] = {
+        "us": ms * 1e3, "TFLOPs": 2.0 * M * N * K / ms / 1e9,
+        "frac_mfma": 2.0 * M * N * K / ms / 1e9 / PEAK_FP8_TFLOPS,
+        "unfused_bf16_gemm_then_act_quant_us": ms2 * 1e3}
+    del qc, scq, cb, qc2, sc2
 
     # activation quantizer 8192x7168, 4 rotated buffer sets (712 MB)
     Mq, Kq = 8192, 7168
@@ -319,7 +343,7 @@ def main():
     if not args.no_parts:
         line["parts"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                              for kk, vv in v.items()}
-                         for k, v in _parts(torch, fp8bs, synth).items()}
+                         for k, v in _parts(torch, fp8bs, synth, (qa, sa, qw, sw)).items()}
     line["cpu_baseline"] = None if args.no_cpu_baseline else _cpu_baseline()
     print(json.dumps(line), flush=True)
 
