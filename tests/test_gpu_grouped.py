@@ -141,3 +141,18 @@ def test_many_groups(fp8bs):
     c = _run(fp8bs, qa, sa, qw, sw, offsets, torch.float32)
     C, B = oracle.block_grouped_gemm(qa, sa, qw, sw, offsets)
     gu.check_gemm(c, C, B)
+
+
+def test_last_round_split_all_outputs(fp8bs):
+    """More tiles than compute units, not a whole number of rounds (22
+    tile-rows x 16 column tiles = 352 on 256 CUs): the tiles of the last
+    partial round run as half-height tiles, some of which are already a
+    group's short last tile-row.  Every output is checked."""
+    sizes = [700, 0, 1500, 129, 1100, 60, 1300]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, N, K = int(offsets[-1]), 4096, 128
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(synth.act(M, K, case=513, tensor=0)))
+    qw, sw = _experts(len(sizes), N, K, 513)
+    c = _run(fp8bs, qa, sa, qw, sw, offsets, torch.float32)
+    C, B = oracle.block_grouped_gemm(qa, sa, qw, sw, offsets)
+    gu.check_gemm(c, C, B)
