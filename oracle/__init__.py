@@ -44,6 +44,7 @@ from .quant import (  # noqa: F401
     quant_w_128x128,
     tile_scale,
 )
+from .delayed import quant_act_1x128_delayed  # noqa: F401
 from .gemm import (  # noqa: F401
     block_gemm,
     block_gemm_e4m3_out,
