@@ -11,6 +11,7 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kTile = 128;
 constexpr int64_t kMaxGroups = 4096;
+constexpr int64_t kMaxHistory = 4096;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -40,6 +41,26 @@ int fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8BS_ERR_LAYOUT;
   return hip_status(fp8bs::launch_quant_act(x, M, K, ldx, q, ldq, s, lds,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quant_act_1x128_delayed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds, int mode,
+                                float* hist, int64_t ldh, int64_t H, int64_t step,
+                                uint32_t* stats, void* stream) {
+  if (mode != FP8BS_DELAY_TILE && mode != FP8BS_DELAY_TENSOR) return FP8BS_ERR_DTYPE;
+  if (M < 0 || K <= 0 || K % kTile != 0 || H < 1 || H > kMaxHistory || step < 0)
+    return FP8BS_ERR_SHAPE;
+  if (M == 0) return FP8BS_OK;
+  if (!x || !q || !s || !hist) return FP8BS_ERR_NULL;
+  if (!ld_ok(ldx, K) || !ld_ok(ldq, K) || lds < M) return FP8BS_ERR_LAYOUT;
+  if (mode == FP8BS_DELAY_TILE && ldh < M) return FP8BS_ERR_LAYOUT;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || !aligned(hist, 4) ||
+      (stats && !aligned(stats, 4)))
+    return FP8BS_ERR_LAYOUT;
+  return hip_status(fp8bs::launch_quant_act_delayed(x, M, K, ldx, q, ldq, s, lds,
+                                                    mode == FP8BS_DELAY_TENSOR, hist, ldh, H,
+                                                    step, stats,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 int fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
@@ -226,7 +247,7 @@ const char* fp8bs_status_string(int status) {
     case FP8BS_ERR_NULL: return "a required pointer is NULL";
     case FP8BS_ERR_SHAPE: return "unsupported shape (negative size, K not a positive multiple of 128, or bad group count)";
     case FP8BS_ERR_LAYOUT: return "unsupported layout (leading dimension or pointer alignment)";
-    case FP8BS_ERR_DTYPE: return "unknown a_kind or out_kind";
+    case FP8BS_ERR_DTYPE: return "unknown a_kind, out_kind or mode";
     case FP8BS_ERR_WORKSPACE: return "workspace missing or too small";
     case FP8BS_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";

@@ -31,6 +31,11 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
                             uint8_t* q, int64_t ldq, float* s, int64_t lds,
                             hipStream_t stream);
 
+hipError_t launch_quant_act_delayed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                    uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                    bool per_tensor, float* hist, int64_t ldh, int64_t H,
+                                    int64_t step, uint32_t* stats, hipStream_t stream);
+
 hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                           uint8_t* q, int64_t ldq, float* s, hipStream_t stream);
 

@@ -18,9 +18,11 @@ OK, ERR_NULL, ERR_SHAPE, ERR_LAYOUT, ERR_DTYPE, ERR_WORKSPACE, ERR_HIP = range(7
 OUT_F32, OUT_BF16 = 0, 1
 A_E4M3, A_BF16 = 0, 1
 OP_QUANT_ACT, OP_QUANT_W, OP_GEMM_E4M3, OP_GEMM_BF16, OP_GROUPED_GEMM = range(5)
+DELAY_TILE, DELAY_TENSOR = 0, 1
 
 EXPORTS = (
     "fp8_quant_act_1x128",
+    "fp8_quant_act_1x128_delayed",
     "fp8_quant_w_128x128",
     "fp8_block_gemm",
     "fp8_block_grouped_gemm",
@@ -38,6 +40,8 @@ _sz = ctypes.c_size_t
 
 _SIGNATURES = {
     "fp8_quant_act_1x128": ([_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _int),
+    "fp8_quant_act_1x128_delayed": ([_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64,
+                                     _i64, _i64, _p, _p], _int),
     "fp8_quant_w_128x128": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p], _int),
     "fp8_block_gemm": ([_int, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _int,
                         _i64, _i64, _i64, _p, _sz, _p], _int),
@@ -129,6 +133,40 @@ def fp8_quant_act_1x128(x, q=None, s=None, lds=None):
     lds = s.shape[1] if s.dim() == 2 else (lds or M)
     _check(lib.fp8_quant_act_1x128(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), lds,
                                    _stream(x)), "fp8_quant_act_1x128")
+    return q, s
+
+
+def fp8_quant_act_1x128_delayed(x, hist, step, mode="tile", q=None, s=None, stats=None):
+    """Delayed (history-based) scaling of bf16 [M][K] per 1x128 tile.
+
+    ``hist``: float32 history ring on the device, updated in place;
+    ``mode="tile"``: [H][K/128][ldh] (ldh >= M), ``mode="tensor"``: [H + 2].
+    ``step``: t = 0, 1, 2, ... in order.  ``stats``: optional int32/uint32 [2]
+    device tensor accumulating (clipped, flushed) counts.
+    Returns ``(q, s)`` as ``fp8_quant_act_1x128``.
+    """
+    _need_device(x, hist, q, s, stats)
+    if x.dtype != torch.bfloat16 or hist.dtype != torch.float32:
+        raise ValueError("x must be bfloat16 and hist float32")
+    M, K = x.shape
+    ldx = _rowmajor(x, "x") if M else K
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(K // 128, M, dtype=torch.float32, device=x.device)
+    if mode == "tile":
+        if hist.dim() != 3:
+            raise ValueError("per-tile history is [H][K/128][ldh]")
+        H, ldh, m = hist.shape[0], hist.shape[2], DELAY_TILE
+    elif mode == "tensor":
+        if hist.dim() != 1:
+            raise ValueError("per-tensor history is [H + 2]")
+        H, ldh, m = hist.shape[0] - 2, 0, DELAY_TENSOR
+    else:
+        raise ValueError("mode must be 'tile' or 'tensor'")
+    _check(lib.fp8_quant_act_1x128_delayed(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s),
+                                           s.shape[1], m, _ptr(hist), ldh, H, step, _ptr(stats),
+                                           _stream(x)), "fp8_quant_act_1x128_delayed")
     return q, s
 
 

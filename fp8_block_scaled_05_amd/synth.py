@@ -54,6 +54,14 @@ def act(M, K, *, case, tensor=0, device="cpu", row_lognormal=True,
     return x.to(torch.bfloat16)
 
 
+def drifting_act(M, K, step, *, case, growth=1.05, device="cpu"):
+    """Activation tensor of training step ``step`` for the online vs delayed
+    scaling comparison: a fresh draw of ``act`` per step (outliers move to
+    new positions) times ``growth ** step`` (the distribution drifts)."""
+    x = act(M, K, case=case, tensor=1000 + step, device=device).float()
+    return (x * float(growth) ** step).to(torch.bfloat16)
+
+
 def weight(N, K, *, case, tensor=1, device="cpu", std=0.02):
     """bf16 [N][K] weight tensor, N(0, std)."""
     g = _gen(device, seed_for(case, tensor))

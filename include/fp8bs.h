@@ -66,6 +66,8 @@ enum { FP8BS_OUT_F32 = 0, FP8BS_OUT_BF16 = 1 };
 /* a_kind: element type of A in fp8_block_gemm. */
 enum { FP8BS_A_E4M3 = 0, FP8BS_A_BF16 = 1 };
 
+/* mode of fp8_quant_act_1x128_delayed: granularity of the history. */
+enum { FP8BS_DELAY_TILE = 0, FP8BS_DELAY_TENSOR = 1 };
 /* op ids for fp8bs_workspace_bytes. */
 enum {
   FP8BS_OP_QUANT_ACT = 0,
@@ -96,6 +98,48 @@ int fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                         uint8_t* q, int64_t ldq, float* s, int64_t lds,
                         void* stream);
 
+/*
+ * Delayed (history-based) scaling of 1x128 activation tiles: the baseline
+ * that online scaling is compared against, for measurement.
+ * Pages: "How online quantization in DeepSeek-V3 differs from delayed
+ * quantization", items 2-4 (delayed quantization takes its scales from the
+ * maxima of earlier iterations, kept in a stored history).
+ *
+ * Step `step` (t >= 0) scales each tile from the largest magnitude over
+ * steps t-H .. t-1 (its window) by the online rule above, with
+ * a = max(window maximum, 2^-64); a tile whose window maximum is 0 (no
+ * history yet) is scaled from its own current maximum.  Values pushed past
+ * the format saturate to +-448.
+ *   mode  FP8BS_DELAY_TILE:   one history per tile position.  hist is a
+ *                             ring of H slots; slot h holds the maxima of a
+ *                             step u with u % H == h, tile (m, kb) at
+ *                             hist[(h*(K/128) + kb)*ldh + m], ldh >= M.
+ *                             The call reads the H slots, then writes this
+ *                             step's maxima into slot t % H.
+ *         FP8BS_DELAY_TENSOR: one history for the whole tensor.  hist is a
+ *                             ring of H + 2 floats; step u in slot
+ *                             u % (H + 2).  The call reads the H window
+ *                             slots, raises slot t % (H + 2) to this step's
+ *                             tensor maximum (atomic max: the slot must hold
+ *                             0 or less) and sets slot (t + 1) % (H + 2) to 0
+ *                             for the next step.  ldh is ignored.
+ *         A history starts as all zeros and is passed to the steps
+ *         t = 0, 1, 2, ... in order, on one stream.
+ *   x, q, s  as fp8_quant_act_1x128 (s receives the scales used).
+ *   stats [in/out] optional uint32[2] (NULL: not counted), accumulated with
+ *         atomic adds: [0] += values clipped by saturation (|x*r| > 464,
+ *         where round-to-nearest would leave the format), [1] += non-zero
+ *         values quantized to a zero code.
+ * M == 0 launches nothing and leaves the history unchanged.
+ * Errors: as fp8_quant_act_1x128; unknown mode -> ERR_DTYPE; H outside
+ *         [1, 4096] or step < 0 -> ERR_SHAPE; hist NULL -> ERR_NULL;
+ *         per-tile ldh < M -> ERR_LAYOUT.
+ */
+int fp8_quant_act_1x128_delayed(const uint16_t* x, int64_t M, int64_t K,
+                                int64_t ldx, uint8_t* q, int64_t ldq,
+                                float* s, int64_t lds, int mode, float* hist,
+                                int64_t ldh, int64_t H, int64_t step,
+                                uint32_t* stats, void* stream);
 /*
  * Online weight quantization, one scale per 128x128 block.
  * Pages: "How online quantization in DeepSeek-V3 differs from delayed

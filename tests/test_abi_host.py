@@ -174,6 +174,28 @@ def test_e4m3_out_validation(fp8bs):
     assert g(qc=P + 8) == fp8bs.ERR_LAYOUT
 
 
+def test_delayed_validation(fp8bs):
+    lib = fp8bs.lib
+
+    def d(x=P, M=64, K=256, ldx=256, q=P, ldq=256, s=P, lds=64, mode=0, hist=P, ldh=64, H=4,
+          step=0, stats=0):
+        return lib.fp8_quant_act_1x128_delayed(x, M, K, ldx, q, ldq, s, lds, mode, hist, ldh, H,
+                                               step, stats, None)
+
+    assert d(mode=2) == fp8bs.ERR_DTYPE
+    assert d(H=0) == fp8bs.ERR_SHAPE
+    assert d(H=5000) == fp8bs.ERR_SHAPE
+    assert d(step=-1) == fp8bs.ERR_SHAPE
+    assert d(K=100) == fp8bs.ERR_SHAPE
+    assert d(M=0, x=0, q=0, s=0, hist=0) == fp8bs.OK
+    assert d(hist=0) == fp8bs.ERR_NULL
+    assert d(ldh=63) == fp8bs.ERR_LAYOUT          # per tile: ldh >= M
+    # per tensor, ldh is not a constraint (the NULL history is what fails)
+    assert d(mode=1, ldh=0, hist=0) == fp8bs.ERR_NULL
+    assert d(stats=P + 2) == fp8bs.ERR_LAYOUT
+    assert d(hist=P + 2) == fp8bs.ERR_LAYOUT
+
+
 def test_workspace_query(fp8bs):
     lib = fp8bs.lib
     assert lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_E4M3, 64, 128, 256, 0) == 0

@@ -1,0 +1,63 @@
+"""GPU parity of delayed (history-based) scaling against the oracle: codes,
+scales, the whole history ring and the clipped/flushed counts, bit for bit,
+over multi-step sequences of drifting activations."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_05_amd import synth
+from tests import _gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp8bs():
+    from fp8_block_scaled_05_amd import fp8bs as mod
+    return mod
+
+
+@pytest.mark.parametrize("mode,H,M,K,ldh_pad,growth", [
+    ("tile", 1, 64, 256, 0, 1.05),
+    ("tile", 4, 70, 384, 6, 1.3),
+    ("tile", 3, 1, 128, 0, 0.8),
+    ("tensor", 1, 64, 256, 0, 1.05),
+    ("tensor", 3, 100, 384, 0, 1.3),
+    ("tensor", 2, 257, 128, 0, 0.7),
+])
+def test_sequence_bit_exact(fp8bs, mode, H, M, K, ldh_pad, growth):
+    KB = K // 128
+    steps = 7
+    if mode == "tile":
+        hist_h = np.zeros((H, KB, M), np.float32)
+        hist_d = torch.zeros(H, KB, M + ldh_pad, dtype=torch.float32, device="cuda")
+    else:
+        hist_h = np.zeros(H + 2, np.float32)
+        hist_d = torch.zeros(H + 2, dtype=torch.float32, device="cuda")
+    stats = torch.zeros(2, dtype=torch.int32, device="cuda")
+    total = np.zeros(2, np.int64)
+    for t in range(steps):
+        x = synth.drifting_act(M, K, t, case=700 + H, growth=growth)
+        q, s = fp8bs.fp8_quant_act_1x128_delayed(x.cuda(), hist_d, t, mode=mode, stats=stats)
+        torch.cuda.synchronize()
+        q_o, s_o, hist_h, st = oracle.quant_act_1x128_delayed(synth.bf16_bits(x), hist_h, t, mode)
+        total += st
+        gu.assert_same_bits(gu.host(q), q_o, f"{mode} step {t} codes")
+        gu.assert_same_bits(gu.host(s), s_o, f"{mode} step {t} scales")
+        hd = gu.host(hist_d)
+        gu.assert_same_bits(hd[:, :, :M] if mode == "tile" else hd, hist_h, f"{mode} step {t} ring")
+        assert np.array_equal(gu.host(stats).astype(np.int64), total), (t, gu.host(stats), total)
+    if growth > 1.2:
+        assert total[0] > 0  # the sequences that grow do clip under delayed scaling
+
+
+def test_stats_are_optional(fp8bs):
+    x = synth.drifting_act(64, 256, 0, case=710)
+    hist = torch.zeros(2, 2, 64, dtype=torch.float32, device="cuda")
+    q, s = fp8bs.fp8_quant_act_1x128_delayed(x.cuda(), hist, 0)
+    torch.cuda.synchronize()
+    q0, s0 = oracle.quant_act_1x128(synth.bf16_bits(x))
+    gu.assert_same_bits(gu.host(q), q0, "codes")
+    gu.assert_same_bits(gu.host(s), s0, "scales")
