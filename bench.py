@@ -13,8 +13,10 @@ path: the activation and weight quantizers alone at 8192x7168 / 18432x7168
 (32 experts, top-8 of 4096 tokens, gate/up and down), the skinny GEMM with
 in-call activation quantization (M = 16, 64), the dense GEMM with its output
 quantized for the next FP8 GEMM (against bf16 output followed by the
-activation quantizer), and the CPU oracle on a bounded sample of the dense
-step (``cpu_baseline``).
+activation quantizer), online against delayed (history-based) scaling on a
+drifting sequence of activations (quantization error, clipped and flushed
+fractions), and the CPU oracle on a bounded sample of the dense step
+(``cpu_baseline``).
 
 The default 300 warm-up steps (about 0.2 s) bring the engine clock to its
 sustained level before the timed steps; with only a few warm-up steps the
@@ -243,7 +245,19 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         "gemms_TFLOPs": (f1 + f2) / (g1 + g2) / 1e9,
         "gemms_frac_mfma": (f1 + f2) / (g1 + g2) / 1e9 / PEAK_FP8_TFLOPS,
         "step_with_quant_us": tot * 1e3, "step_TFLOPs": (f1 + f2) / tot / 1e9}
+
+    # online vs delayed scaling on drifting activations (quality, not speed)
+    from fp8_block_scaled_05_amd import ablation
+    out["online_vs_delayed_scaling_M4096_K7168"] = ablation.run(steps=24, timing_iters=10)
     return out
+
+
+def _rounded(v):
+    if isinstance(v, dict):
+        return {k: _rounded(x) for k, x in v.items()}
+    if isinstance(v, float):
+        return float(f"{v:.5g}")
+    return v
 
 
 def _cpu_baseline():
@@ -341,9 +355,7 @@ def main():
                               "frac_hbm": round(act_bytes / qa_ms / 1e6 / PEAK_HBM_GBPS, 4)},
     }
     if not args.no_parts:
-        line["parts"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
-                             for kk, vv in v.items()}
-                         for k, v in _parts(torch, fp8bs, synth, (qa, sa, qw, sw)).items()}
+        line["parts"] = _rounded(_parts(torch, fp8bs, synth, (qa, sa, qw, sw)))
     line["cpu_baseline"] = None if args.no_cpu_baseline else _cpu_baseline()
     print(json.dumps(line), flush=True)
 

@@ -7,13 +7,17 @@
 // The scale of step t comes from the largest magnitude over steps t-H..t-1,
 // by the online scale rule; a group with an empty window (maximum 0) is
 // scaled from its current maximum.  Two granularities:
-//   per tile:   ring hist[H][KB][ldh], step u in slot u % H; each 16-lane row
-//               reads its tile's H slots, then stores its current maximum in
-//               slot t % H (the tile has one owner, so no race);
+//   per tile:   ring hist[H][KB][ldh], step u in slot u % H; the 16 lanes of
+//               a tile's row read its H slots, 16 at a time, and reduce them
+//               by DPP max; lane 0 then stores the current maximum in slot
+//               t % H (the tile has one owner, so no race);
 //   per tensor: ring hist[H + 2], step u in slot u % (H + 2); every workgroup
 //               reads the H window slots, raises slot t % (H + 2) to its
 //               maximum with an atomic max, and clears slot (t + 1) % (H + 2)
-//               for the next step (no slot is both read and written).
+//               for the next step (no slot is both read and written).  The
+//               atomics of all workgroups meet at one address, so a
+//               workgroup first reads the slot and skips the atomic when its
+//               maximum cannot raise it (the slot only grows during a step).
 // Values that the stale scale pushes past the format saturate; clipped
 // (|x r| > 464, where round-to-nearest would leave the format) and flushed
 // (non-zero, zero code) values are counted with one atomic add per wave.
@@ -102,7 +106,11 @@ __global__ __launch_bounds__(256) void quant_act_delayed_kernel(DelayArgs a) {
     const float cur = max_row16(absmax8(v[i], 0.0f));
     float win = win_tensor;
     if constexpr (!TENSOR) {
-      for (int64_t h = 0; h < a.H; ++h) win = fmaxf(win, a.hist[(h * a.KB + kb) * a.ldh + mc]);
+      for (int64_t h0 = 0; h0 < a.H; h0 += 16) {
+        const int64_t h = h0 + lane;
+        win = fmaxf(win, h < a.H ? a.hist[(h * a.KB + kb) * a.ldh + mc] : 0.0f);
+      }
+      win = max_row16(win);
     }
     float sc, r;
     group_scale(win > 0.0f ? win : cur, sc, r);
@@ -127,7 +135,9 @@ __global__ __launch_bounds__(256) void quant_act_delayed_kernel(DelayArgs a) {
     if (threadIdx.x == 0) {
       const float wmax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
       // non-negative floats order like their bit patterns
-      atomicMax(reinterpret_cast<unsigned int*>(a.hist + a.step % ring), __float_as_uint(wmax));
+      unsigned int* const slot = reinterpret_cast<unsigned int*>(a.hist + a.step % ring);
+      if (__float_as_uint(wmax) > __atomic_load_n(slot, __ATOMIC_RELAXED))
+        atomicMax(slot, __float_as_uint(wmax));
       a.hist[(a.step + 1) % ring] = 0.0f;
     }
   }

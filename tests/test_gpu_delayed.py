@@ -61,3 +61,17 @@ def test_stats_are_optional(fp8bs):
     q0, s0 = oracle.quant_act_1x128(synth.bf16_bits(x))
     gu.assert_same_bits(gu.host(q), q0, "codes")
     gu.assert_same_bits(gu.host(s), s0, "scales")
+
+
+def test_ablation_runner_small(fp8bs):
+    """The online vs delayed comparison runs end to end on a small case;
+    online scaling never clips, and its error is no larger than the
+    delayed methods' on a growing sequence."""
+    from fp8_block_scaled_05_amd import ablation
+    r = ablation.run(steps=8, M=256, K=512, H=2, growths=(1.3,), timing_iters=2)
+    sc = r["scenarios"]["growth_1.3"]
+    assert sc["online"]["clipped_frac"] == 0.0
+    assert sc["delayed_tile"]["clipped_frac"] > 0.0 and sc["delayed_tensor"]["clipped_frac"] > 0.0
+    assert sc["online"]["rel_rmse"] <= min(sc["delayed_tile"]["rel_rmse"],
+                                           sc["delayed_tensor"]["rel_rmse"])
+    assert set(r["throughput"]) == {"online", "delayed_tile", "delayed_tensor"}
