@@ -44,6 +44,13 @@ from .quant import (  # noqa: F401
     quant_w_128x128,
     tile_scale,
 )
+from .backward import (  # noqa: F401
+    block_gemm_rowscaled,
+    dgrad,
+    quant_act_128x1_t,
+    quant_w_128x128_t,
+    wgrad,
+)
 from .delayed import quant_act_1x128_delayed  # noqa: F401
 from .gemm import (  # noqa: F401
     block_gemm,
