@@ -70,8 +70,33 @@ int fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, ui
   if (!w || !q || !s) return FP8BS_ERR_NULL;
   if (!ld_ok(ldw, K) || !ld_ok(ldq, K)) return FP8BS_ERR_LAYOUT;
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8BS_ERR_LAYOUT;
-  return hip_status(
-      fp8bs::launch_quant_w(w, N, K, ldw, q, ldq, s, static_cast<hipStream_t>(stream)));
+  return hip_status(fp8bs::launch_quant_w(w, N, K, ldw, q, ldq, s, nullptr, 0, nullptr,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quant_act_128x1_t(const uint16_t* x, int64_t M, int64_t N, int64_t ldx, uint8_t* qt,
+                          int64_t ldqt, float* st, int64_t ldst, void* stream) {
+  if (M < 0 || N < 0 || M % kTile != 0 || N % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!x || !qt || !st) return FP8BS_ERR_NULL;
+  if (!ld_ok(ldx, N) || !ld_ok(ldqt, M) || ldst < N) return FP8BS_ERR_LAYOUT;
+  if (!aligned(x, 16) || !aligned(qt, 16) || !aligned(st, 4)) return FP8BS_ERR_LAYOUT;
+  return hip_status(fp8bs::launch_quant_act_128x1_t(x, M, N, ldx, qt, ldqt, st, ldst,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quant_w_128x128_t(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                          int64_t ldq, float* s, uint8_t* qt, int64_t ldqt, float* st,
+                          void* stream) {
+  if (N < 0 || K <= 0 || K % kTile != 0 || N % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (N == 0) return FP8BS_OK;
+  if (!w || !q || !s || !qt || !st) return FP8BS_ERR_NULL;
+  if (!ld_ok(ldw, K) || !ld_ok(ldq, K) || !ld_ok(ldqt, N)) return FP8BS_ERR_LAYOUT;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4) || !aligned(qt, 16) ||
+      !aligned(st, 4))
+    return FP8BS_ERR_LAYOUT;
+  return hip_status(fp8bs::launch_quant_w(w, N, K, ldw, q, ldq, s, qt, ldqt, st,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
@@ -201,6 +226,38 @@ int fp8_block_gemm_e4m3_out(int a_kind, const void* a, int64_t lda, float* sa, i
                             int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   return block_gemm_impl(a_kind, a, lda, sa, ldsa, b, ldb, sb, qc, ldqc, fp8bs::kOutE4M3, sc,
                          ldsc, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int fp8_block_gemm_rowscaled(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                             const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
+                             void* c, int64_t ldc, int out_kind, int64_t M, int64_t N, int64_t K,
+                             void* stream) {
+  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || K % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!a || !sa || !b || !sb || !c) return FP8BS_ERR_NULL;
+  if (!ld_ok(lda, K) || !ld_ok(ldb, K) || ldc < N || ldsa < M || ldsb < N)
+    return FP8BS_ERR_LAYOUT;
+  const uintptr_t c_align = out_kind == FP8BS_OUT_F32 ? 4 : 2;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sa, 4) ||
+      !aligned(sb, 4))
+    return FP8BS_ERR_LAYOUT;
+  fp8bs::GemmArgs g{};
+  g.a = a;
+  g.lda = lda;
+  g.sa = sa;
+  g.ldsa = ldsa;
+  g.b = b;
+  g.ldb = ldb;
+  g.sb = sb;
+  g.sb_ld = ldsb;
+  g.c = c;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return hip_status(fp8bs::launch_block_gemm_rowscaled(g, out_of(out_kind),
+                                                       static_cast<hipStream_t>(stream)));
 }
 
 int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,

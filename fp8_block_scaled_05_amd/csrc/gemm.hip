@@ -14,6 +14,7 @@
 //   read once; 1 wave along M; four LDS stages (three K groups in flight).
 //   E4M3 output (quantized per 128 output columns) needs tiles of whole
 //   128-column groups, so it takes the 64x128 tile for every M <= 64.
+// The weight-gradient GEMM (B scaled per row and K group) uses the same tiles.
 
 #include "gemm_kernel.hpp"
 
@@ -35,6 +36,13 @@ hipError_t launch_block_gemm(const GemmArgs& args, OutKind out, hipStream_t stre
   if (args.M <= 32 && out != kOutE4M3) return gemm::launch<Rows32Cfg, false>(args, out, stream);
   if (args.M <= 64) return gemm::launch<Rows64Cfg, false>(args, out, stream);
   return gemm::launch<LargeCfg, false, LargeTail>(args, out, stream);
+}
+
+hipError_t launch_block_gemm_rowscaled(const GemmArgs& args, OutKind out, hipStream_t stream) {
+  using gemm::RowScaledB;
+  if (args.M <= 32) return gemm::launch<RowScaledB<Rows32Cfg>, false>(args, out, stream);
+  if (args.M <= 64) return gemm::launch<RowScaledB<Rows64Cfg>, false>(args, out, stream);
+  return gemm::launch<RowScaledB<LargeCfg>, false, RowScaledB<LargeTail>>(args, out, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, OutKind out, hipStream_t stream) {

@@ -50,6 +50,8 @@ struct Cfg {
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 MFMA tiles per wave
   // weight-block scales of the tile: one per 128 columns
   static constexpr int SB_COUNT = (BN + 127) / 128;
+  // B scales per 128x128 block (false) or per row and K group (RowScaledB)
+  static constexpr bool ROWB = false;
   // LDS stage: A rows | B rows; the scales of a stage live in a separate
   // array (activation scales, then weight-block scales) so that the compiler
   // can tell their register->LDS writes from the in-flight tile copies
@@ -59,9 +61,11 @@ struct Cfg {
   // 1 KB (8 rows) per wave-wide direct load
   static constexpr int TILE_LOADS = (BM + BN) / 8 / NWAVES;
   // the scales go through registers (one fp32 per thread per item: the BM
-  // activation scales, then the SB_COUNT weight-block scales of the tile)
-  // and are written to LDS after the compute; SREG loads per thread per stage
-  static constexpr int SCALE_ITEMS = BM + SB_COUNT;
+  // activation scales, then the SB_COUNT weight-block scales of the tile, or
+  // with row-scaled B its BN row scales) and are written to LDS after the
+  // compute; SREG loads per thread per stage (room for BN B scales in both
+  // cases: the block case repeats its last scale in the spare slots)
+  static constexpr int SCALE_ITEMS = BM + BN;
   static constexpr int SREG = (SCALE_ITEMS + THREADS - 1) / THREADS;
   // every thread writes its SREG slots (no branch, so no merged wait counts)
   static constexpr int SCALE_FLOATS = SREG * THREADS;
@@ -72,6 +76,15 @@ struct Cfg {
   static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS <= 63, "vmcnt range");
+};
+
+// The same tile configuration with B scaled per row and 128-K group (one
+// scale per column of C per group, like the activation tiles of A) instead of
+// per 128x128 block: the weight-gradient GEMM dW = dY^T . X, whose operands
+// are both token-grouped activations.
+template <class C>
+struct RowScaledB : C {
+  static constexpr bool ROWB = true;
 };
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
@@ -228,6 +241,10 @@ __device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t
     const int item = (int)threadIdx.x + s * C::THREADS;
     if (item < C::BM) {
       lp.scale[s] = item < rows_a ? item : rows_a - 1;
+    } else if constexpr (C::ROWB) {
+      // row scale of tile column j (columns past N repeat the last)
+      const int j = item - C::BM;
+      lp.scale[s] = j < rows_b ? j : rows_b - 1;
     } else {
       // weight-block scale j of the tile (items past the end repeat the last)
       const int64_t nbl = NB - 1 - t.col0 / 128;  // last block index within the tile
@@ -281,7 +298,7 @@ __device__ __forceinline__ void load_scales(const GemmArgs& p, const TileCoords&
                                             const LoadPlan<C>& lp, int64_t kb,
                                             float (&v)[C::SREG]) {
   const float* sa = p.sa + kb * p.ldsa + t.row0;
-  const float* sb = t.sb + (t.col0 / 128) * p.sb_ld + kb;
+  const float* sb = C::ROWB ? t.sb + kb * p.sb_ld + t.col0 : t.sb + (t.col0 / 128) * p.sb_ld + kb;
 #pragma unroll
   for (int s = 0; s < C::SREG; ++s) {
     const int item = (int)threadIdx.x + s * C::THREADS;
@@ -317,6 +334,7 @@ struct FragOffs {
   int a_lo, a_hi, b_lo, b_hi;  // K chunks 2g and 2g+1 of lane group g
   int sa;                      // float index of the lane's first activation scale
   int sv;                      // float index of the scales this lane loads for its row of 16
+  int sbc;                     // row-scaled B: float index of the lane's first column scale
 };
 
 template <class C>
@@ -342,6 +360,8 @@ __device__ __forceinline__ FragOffs frag_offsets(int wm, int wn, int lane) {
   } else {
     f.sv = f.sa;
   }
+  // the lane's FN output columns are consecutive (permuted B staging)
+  f.sbc = C::BM + wn * C::TN + C::FN * l16;
   asm volatile("" : "+v"(f.a_lo), "+v"(f.a_hi), "+v"(f.b_lo), "+v"(f.b_hi), "+v"(f.sa),
                "+v"(f.sv));
   return f;
@@ -373,7 +393,26 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   // they have a whole step of slack and are spread over all rows.
   constexpr int ISSUE_ROWS = C::STAGES == 2 ? (C::FM + 1) / 2 : C::FM;
   constexpr int PER_ROW = (C::TILE_LOADS + ISSUE_ROWS - 1) / ISSUE_ROWS;
-  const float sbv = sc[C::BM + (wn * C::TN) / 128];
+  // block-scaled B: one weight-block scale for the wave's columns, folded
+  // into the row factors; row-scaled B: the lane's FN column scales, applied
+  // per MFMA tile
+  const float sbv = C::ROWB ? 1.0f : sc[C::BM + (wn * C::TN) / 128];
+  float sbj[C::FN];
+  if constexpr (C::ROWB) {
+    if constexpr (C::FN % 4 == 0) {
+#pragma unroll
+      for (int q = 0; q < C::FN / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(sc + fo.sbc + 4 * q);
+        sbj[4 * q] = v.x;
+        sbj[4 * q + 1] = v.y;
+        sbj[4 * q + 2] = v.z;
+        sbj[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < C::FN; ++q) sbj[q] = sc[fo.sbc + q];
+    }
+  }
   const float* w4 = sc + fo.sa;
   // FM % 4 == 0: each lane holds PV of its row's activation scales (one LDS
   // read per group instead of one 16-byte read per MFMA row) and the
@@ -405,8 +444,10 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
     if (t >= RING) {
       const int u = t - RING, i = u / C::FN, j = u % C::FN;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        acc[i][j][r] = __builtin_fmaf(ring[u % RING][r], w[i % WS][r], acc[i][j][r]);
+      for (int r = 0; r < 4; ++r) {
+        const float f = C::ROWB ? w[i % WS][r] * sbj[j] : w[i % WS][r];
+        acc[i][j][r] = __builtin_fmaf(ring[u % RING][r], f, acc[i][j][r]);
+      }
     }
     if (t < NM) {
       const int i = t / C::FN, j = t % C::FN;
@@ -828,11 +869,13 @@ hipError_t launch(const GemmArgs& args, OutKind out, hipStream_t stream) {
                          args, full);
       break;
     default:
-      if constexpr (C::BN % 128 == 0) {
+      if constexpr (C::BN % 128 == 0 && !C::ROWB) {
         hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, kOutE4M3>), grid, block, 0,
                            stream, args, full);
       } else {
-        return hipErrorInvalidConfiguration;  // E4M3 output needs whole 128-column tiles
+        // E4M3 output needs whole 128-column tiles; row-scaled B (weight
+        // gradients) has fp32 and bf16 outputs only
+        return hipErrorInvalidConfiguration;
       }
       break;
   }

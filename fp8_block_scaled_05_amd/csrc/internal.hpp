@@ -15,7 +15,8 @@ struct GemmArgs {
   int64_t ldb;
   int64_t b_group_stride;  // bytes between experts' weights (grouped only)
   const float* sb;
-  int64_t sb_ld;  // floats between consecutive 128-row bands of S_W (= K/128 of the whole GEMM)
+  int64_t sb_ld;  // block-scaled B: floats between consecutive 128-row bands of S_W (= K/128);
+                  // row-scaled B: floats between consecutive K groups' rows of scales
   void* c;       // output: fp32, bf16 or E4M3 codes [M][ldc]
   int64_t ldc;
   float* sc;     // E4M3 output only: scale of row m, 128-column block nb at sc[nb*ldsc + m]
@@ -36,13 +37,23 @@ hipError_t launch_quant_act_delayed(const uint16_t* x, int64_t M, int64_t K, int
                                     bool per_tensor, float* hist, int64_t ldh, int64_t H,
                                     int64_t step, uint32_t* stats, hipStream_t stream);
 
+// M and N multiples of 128
+hipError_t launch_quant_act_128x1_t(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
+                                    uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
+                                    hipStream_t stream);
+
+// qt == nullptr: no transposed output
 hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
-                          uint8_t* q, int64_t ldq, float* s, hipStream_t stream);
+                          uint8_t* q, int64_t ldq, float* s, uint8_t* qt, int64_t ldqt,
+                          float* st, hipStream_t stream);
 
 // Output element type of the GEMM kernels.
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2 };
 
 hipError_t launch_block_gemm(const GemmArgs& args, OutKind out, hipStream_t stream);
+
+// B scaled per row and 128-K group: sb(n, kb) at sb[kb*sb_ld + n]
+hipError_t launch_block_gemm_rowscaled(const GemmArgs& args, OutKind out, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, OutKind out, hipStream_t stream);
 

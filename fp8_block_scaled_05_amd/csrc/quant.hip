@@ -52,12 +52,40 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
   }
 }
 
+// Transpose of an 8x8 byte block: row i is (lo[i], hi[i]) (bytes 0..3, 4..7);
+// returns column c as (olo[c], ohi[c]) = bytes c of rows 0..3 and 4..7.
+// v_perm_b32 picks each result byte from the 8 bytes {S0 (4..7), S1 (0..3)}.
+__device__ __forceinline__ void transpose8x8(const uint32_t (&lo)[8], const uint32_t (&hi)[8],
+                                             uint32_t (&olo)[8], uint32_t (&ohi)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t (&src)[8] = c < 4 ? lo : hi;
+    const uint32_t b = (uint32_t)(c & 3);
+    const uint32_t pick = b | ((4u + b) << 8);  // byte b of S1, then byte b of S0
+    const uint32_t r01 = __builtin_amdgcn_perm(src[1], src[0], pick);
+    const uint32_t r23 = __builtin_amdgcn_perm(src[3], src[2], pick);
+    const uint32_t r45 = __builtin_amdgcn_perm(src[5], src[4], pick);
+    const uint32_t r67 = __builtin_amdgcn_perm(src[7], src[6], pick);
+    olo[c] = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+    ohi[c] = __builtin_amdgcn_perm(r67, r45, 0x05040100u);
+  }
+}
+
 // grid: one workgroup per 128x128 block, K group fastest.  Each thread holds
 // 8 row segments of 8 values (the block stays in registers: one HBM pass).
+// TRANS: the codes are also written transposed (qt [K][ldqt], N contiguous)
+// with the transposed scale grid st [K/128][N/128], the B operand of the
+// data-gradient GEMM dX = dY . W.  The block's codes go through LDS; each
+// thread then reads an 8x8 byte block, transposes it in registers and writes
+// eight 8-byte row pieces of qt.
+template <bool TRANS>
 __global__ __launch_bounds__(256) void quant_w_128x128_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t KB, int64_t ldw,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s) {
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, uint8_t* __restrict__ qt,
+    int64_t ldqt, float* __restrict__ st) {
   __shared__ float wave_max[4];
+  constexpr int kPitch = 136;  // LDS row pitch of the staged codes (bytes)
+  __shared__ __attribute__((aligned(16))) uint8_t tile[TRANS ? 128 * kPitch : 8];
   const int64_t bid = blockIdx.x;
   const int64_t kb = bid % KB;
   const int64_t nb = bid / KB;
@@ -86,15 +114,137 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t n = nb * 128 + r0 + 16 * i;
-    if (n < N) {
-      const u32x2 codes = quant8(v[i], r);
+    const u32x2 codes = quant8(v[i], r);
+    if (n < N)
       __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + n * ldq + kb * 128) + lane);
-    }
+    if constexpr (TRANS)
+      *reinterpret_cast<u32x2*>(tile + (r0 + 16 * i) * kPitch + lane * 8) = codes;
   }
   if (threadIdx.x == 0) s[nb * KB + kb] = sc;
+  if constexpr (TRANS) {
+    // N % 128 == 0 here: every row of the block is real
+    __syncthreads();
+    const int n0 = (threadIdx.x & 15) * 8, k0 = (threadIdx.x >> 4) * 8;
+    uint32_t lo[8], hi[8], olo[8], ohi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x2 d = *reinterpret_cast<const u32x2*>(tile + (n0 + i) * kPitch + k0);
+      lo[i] = d.x;
+      hi[i] = d.y;
+    }
+    transpose8x8(lo, hi, olo, ohi);
+    const int64_t NB = N / 128;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int64_t k = kb * 128 + k0 + c;
+      __builtin_nontemporal_store(u32x2{olo[c], ohi[c]},
+                                  reinterpret_cast<u32x2*>(qt + k * ldqt + nb * 128 + n0));
+    }
+    if (threadIdx.x == 0) st[kb * NB + nb] = sc;
+  }
+}
+
+// Groups of 128 consecutive rows per column (the 1x128 tiles of x^T), the
+// operands of the weight-gradient GEMM dW = dY^T . X, which contracts over
+// the tokens.  One workgroup per 128x128 block (N block fastest); each
+// thread holds 8 row pieces of 8 values.  Column maxima: over the thread's
+// rows, across the 4 row groups of a wave by shuffles, across the 4 waves
+// in LDS; one thread per column forms its scale and reciprocal.  The codes
+// are staged in LDS and written transposed (qt [N][M]) in 8x8 byte blocks.
+__global__ __launch_bounds__(256) void quant_act_128x1_t_kernel(
+    const uint16_t* __restrict__ x, int64_t NB, int64_t ldx, uint8_t* __restrict__ qt,
+    int64_t ldqt, float* __restrict__ st, int64_t ldst) {
+  constexpr int kPitch = 136;
+  __shared__ float colmax[4][128];
+  __shared__ __attribute__((aligned(16))) float rcp[128];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kPitch];
+  const int64_t bid = blockIdx.x;
+  const int64_t nb = bid % NB;
+  const int64_t mb = bid / NB;
+  const int lane = threadIdx.x & 15;
+  const int r0 = threadIdx.x >> 4;
+
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+               x + (mb * 128 + r0 + 16 * i) * ldx + nb * 128) + lane);
+  float cm[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) cm[c] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 d = v[i];
+    cm[0] = fmaxf(cm[0], fabsf(bf16_lo(d.x)));
+    cm[1] = fmaxf(cm[1], fabsf(bf16_hi(d.x)));
+    cm[2] = fmaxf(cm[2], fabsf(bf16_lo(d.y)));
+    cm[3] = fmaxf(cm[3], fabsf(bf16_hi(d.y)));
+    cm[4] = fmaxf(cm[4], fabsf(bf16_lo(d.z)));
+    cm[5] = fmaxf(cm[5], fabsf(bf16_hi(d.z)));
+    cm[6] = fmaxf(cm[6], fabsf(bf16_lo(d.w)));
+    cm[7] = fmaxf(cm[7], fabsf(bf16_hi(d.w)));
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    cm[c] = fmaxf(cm[c], __shfl_xor(cm[c], 16, 64));
+    cm[c] = fmaxf(cm[c], __shfl_xor(cm[c], 32, 64));
+  }
+  if ((threadIdx.x & 63) < 16) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) colmax[threadIdx.x >> 6][lane * 8 + c] = cm[c];
+  }
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int col = threadIdx.x;
+    const float amax = fmaxf(fmaxf(colmax[0][col], colmax[1][col]),
+                             fmaxf(colmax[2][col], colmax[3][col]));
+    float sc, r;
+    group_scale(amax, sc, r);
+    rcp[col] = r;
+    st[mb * ldst + nb * 128 + col] = sc;
+  }
+  __syncthreads();
+  const float4 ra = *reinterpret_cast<const float4*>(rcp + lane * 8);
+  const float4 rb = *reinterpret_cast<const float4*>(rcp + lane * 8 + 4);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 d = v[i];
+    uint32_t lo = cvt2_e4m3<false>(bf16_lo(d.x) * ra.x, bf16_hi(d.x) * ra.y, 0u);
+    lo = cvt2_e4m3<true>(bf16_lo(d.y) * ra.z, bf16_hi(d.y) * ra.w, lo);
+    uint32_t hi = cvt2_e4m3<false>(bf16_lo(d.z) * rb.x, bf16_hi(d.z) * rb.y, 0u);
+    hi = cvt2_e4m3<true>(bf16_lo(d.w) * rb.z, bf16_hi(d.w) * rb.w, hi);
+    *reinterpret_cast<u32x2*>(tile + (r0 + 16 * i) * kPitch + lane * 8) = u32x2{lo, hi};
+  }
+  __syncthreads();
+  const int c0 = (threadIdx.x & 15) * 8, m0 = (threadIdx.x >> 4) * 8;
+  uint32_t lo[8], hi[8], olo[8], ohi[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x2 d = *reinterpret_cast<const u32x2*>(tile + (m0 + i) * kPitch + c0);
+    lo[i] = d.x;
+    hi[i] = d.y;
+  }
+  transpose8x8(lo, hi, olo, ohi);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int64_t n = nb * 128 + c0 + c;
+    __builtin_nontemporal_store(u32x2{olo[c], ohi[c]},
+                                reinterpret_cast<u32x2*>(qt + n * ldqt + mb * 128 + m0));
+  }
 }
 
 }  // namespace
+
+hipError_t launch_quant_act_128x1_t(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
+                                    uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
+                                    hipStream_t stream) {
+  const int64_t NB = N / 128;
+  const int64_t blocks = (M / 128) * NB;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_act_128x1_t_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                     NB, ldx, qt, ldqt, st, ldst);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             uint8_t* q, int64_t ldq, float* s, int64_t lds,
@@ -109,13 +259,19 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 }
 
 hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
-                          uint8_t* q, int64_t ldq, float* s, hipStream_t stream) {
+                          uint8_t* q, int64_t ldq, float* s, uint8_t* qt, int64_t ldqt,
+                          float* st, hipStream_t stream) {
   const int64_t KB = K / 128;
   const int64_t NB = (N + 127) / 128;
   const int64_t blocks = NB * KB;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(quant_w_128x128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     w, N, KB, ldw, q, ldq, s);
+  if (qt) {
+    hipLaunchKernelGGL(quant_w_128x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, w, N, KB, ldw, q, ldq, s, qt, ldqt, st);
+  } else {
+    hipLaunchKernelGGL(quant_w_128x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, w, N, KB, ldw, q, ldq, s, qt, ldqt, st);
+  }
   return hipGetLastError();
 }
 

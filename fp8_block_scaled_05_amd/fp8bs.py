@@ -23,11 +23,14 @@ DELAY_TILE, DELAY_TENSOR = 0, 1
 EXPORTS = (
     "fp8_quant_act_1x128",
     "fp8_quant_act_1x128_delayed",
+    "fp8_quant_act_128x1_t",
     "fp8_quant_w_128x128",
+    "fp8_quant_w_128x128_t",
     "fp8_block_gemm",
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_e4m3_out",
     "fp8_block_grouped_gemm_e4m3_out",
+    "fp8_block_gemm_rowscaled",
     "fp8bs_workspace_bytes",
     "fp8bs_status_string",
     "fp8bs_last_hip_error",
@@ -43,6 +46,10 @@ _SIGNATURES = {
     "fp8_quant_act_1x128_delayed": ([_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64,
                                      _i64, _i64, _p, _p], _int),
     "fp8_quant_w_128x128": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p], _int),
+    "fp8_quant_w_128x128_t": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p], _int),
+    "fp8_quant_act_128x1_t": ([_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _int),
+    "fp8_block_gemm_rowscaled": ([_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _int, _i64,
+                                  _i64, _i64, _p], _int),
     "fp8_block_gemm": ([_int, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _int,
                         _i64, _i64, _i64, _p, _sz, _p], _int),
     "fp8_block_grouped_gemm": ([_p, _i64, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _int,
@@ -184,6 +191,59 @@ def fp8_quant_w_128x128(w, q=None, s=None):
     _check(lib.fp8_quant_w_128x128(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _stream(w)),
            "fp8_quant_w_128x128")
     return q, s
+
+
+def fp8_quant_w_128x128_t(w, q=None, s=None, qt=None, st=None):
+    """bf16 [N][K] -> (q [N][K], s [N/128][K/128], qt [K][N], st [K/128][N/128]):
+    the weight's codes and scales for the forward GEMM and, transposed, for
+    the data-gradient GEMM dX = dY . W (``fp8_block_gemm(qdy, sdy, qt, st)``)."""
+    _need_device(w, q, s, qt, st)
+    if w.dtype != torch.bfloat16:
+        raise ValueError("w must be bfloat16")
+    N, K = w.shape
+    ldw = _rowmajor(w, "w") if N else K
+    dev = w.device
+    q = torch.empty(N, K, dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty(N // 128, K // 128, dtype=torch.float32, device=dev) if s is None else s
+    qt = torch.empty(K, N, dtype=torch.uint8, device=dev) if qt is None else qt
+    st = torch.empty(K // 128, N // 128, dtype=torch.float32, device=dev) if st is None else st
+    _check(lib.fp8_quant_w_128x128_t(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _ptr(qt),
+                                     _ld(qt), _ptr(st), _stream(w)), "fp8_quant_w_128x128_t")
+    return q, s, qt, st
+
+
+def fp8_quant_act_128x1_t(x, qt=None, st=None):
+    """bf16 [M][N] -> (qt uint8 [N][M], st fp32 [M/128][N]): groups of 128
+    consecutive rows per column, codes transposed (the operands of the
+    weight-gradient GEMM)."""
+    _need_device(x, qt, st)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    M, N = x.shape
+    ldx = _rowmajor(x, "x") if M else N
+    if qt is None:
+        qt = torch.empty(N, M, dtype=torch.uint8, device=x.device)
+    if st is None:
+        st = torch.empty(M // 128, N, dtype=torch.float32, device=x.device)
+    _check(lib.fp8_quant_act_128x1_t(_ptr(x), M, N, ldx, _ptr(qt), _ld(qt), _ptr(st),
+                                     st.shape[1], _stream(x)), "fp8_quant_act_128x1_t")
+    return qt, st
+
+
+def fp8_block_gemm_rowscaled(a, sa, b, sb, out=None, out_dtype=torch.float32):
+    """C[M][N] = A . B^T with one scale per row and 128-K group on both
+    operands (sa [K/128][ldsa], sb [K/128][ldsb]); the weight-gradient GEMM
+    dW = dY^T . X with (a, sa), (b, sb) from ``fp8_quant_act_128x1_t``."""
+    _need_device(a, sa, b, sb, out)
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    _check(lib.fp8_block_gemm_rowscaled(_ptr(a), _ld(a), _ptr(sa), sa.shape[1], _ptr(b), _ld(b),
+                                        _ptr(sb), sb.shape[1], _ptr(out), _ld(out),
+                                        _out_kind(out.dtype), M, N, K, _stream(a)),
+           "fp8_block_gemm_rowscaled")
+    return out
 
 
 def _out_kind(dtype):

@@ -158,6 +158,50 @@ int fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                         uint8_t* q, int64_t ldq, float* s, void* stream);
 
 /*
+ * Quantization in groups of 128 consecutive rows per column, with the codes
+ * written transposed: the operands of the weight-gradient GEMM
+ * dW[N][K] = dY^T . X of the backward pass, which contracts over the M
+ * tokens (both dY [M][N] and X [M][K] go through this call).
+ * Pages: "How the unified E4M3 format adds to DeepSeek-V3's efficiency",
+ * section "Fine-grained quantization strategy" (E4M3 with fine-grained
+ * groups in every stage of training); reading: groups of 128 along the
+ * GEMM's contraction dimension, so these are the 1x128 tiles of x^T,
+ * quantized by the online rule.
+ *
+ *   x   [in]  bf16 bit patterns [M][ldx], ldx >= N.
+ *   qt  [out] E4M3 codes of x^T, [N][ldqt] (row n holds x[0..M-1][n]);
+ *             ldqt >= M, a multiple of 16; 16-byte aligned.
+ *   st  [out] fp32 scales: st(n, mb) at st[mb*ldst + n], ldst >= N (the
+ *             activation-scale layout for a GEMM whose rows are the n).
+ * Errors: M or N not a multiple of 128 -> ERR_SHAPE; as
+ *         fp8_quant_act_1x128 otherwise.
+ */
+int fp8_quant_act_128x1_t(const uint16_t* x, int64_t M, int64_t N,
+                          int64_t ldx, uint8_t* qt, int64_t ldqt, float* st,
+                          int64_t ldst, void* stream);
+/*
+ * fp8_quant_w_128x128 that also writes the codes transposed, the B operand
+ * of the data-gradient GEMM dX = dY . W of the backward pass (there the
+ * contraction runs over N).  The 128x128 blocks and their scales are the same
+ * for W and W^T; only the layouts change.
+ * Pages: "How the unified E4M3 format adds to DeepSeek-V3's efficiency",
+ * section "Fine-grained quantization strategy" (E4M3 with the same
+ * fine-grained groups in every stage of training, the backward pass
+ * included); reading: the groups stay 128x128 blocks of W.
+ *
+ *   w, q, s  as fp8_quant_w_128x128 (N must be a multiple of 128).
+ *   qt  [out] E4M3 codes of W^T, [K][ldqt] (row k holds W[0..N-1][k]);
+ *             ldqt >= N, a multiple of 16; 16-byte aligned.
+ *   st  [out] fp32 scales of W^T's blocks, row-major [K/128][N/128]:
+ *             st[kb*(N/128) + nb] = s[nb*(K/128) + kb].
+ *   (qt, st) is the (b, sb) of fp8_block_gemm for dX[M][K] = dY[M][N] . W,
+ *   with the GEMM's contraction length N.
+ * Errors: as fp8_quant_w_128x128; N % 128 != 0 -> ERR_SHAPE.
+ */
+int fp8_quant_w_128x128_t(const uint16_t* w, int64_t N, int64_t K,
+                          int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                          uint8_t* qt, int64_t ldqt, float* st, void* stream);
+/*
  * Block-scaled FP8 GEMM with FP32 promotion every 128 K:  C = A . B^T.
  * Pages: "Advantages of using FP8 for GEMM operations in DeepSeek-V3",
  * items 1, 5 and 8 (FP8 GEMM; partial sums promoted to FP32 registers at
@@ -211,6 +255,29 @@ int fp8_block_gemm_e4m3_out(int a_kind, const void* a, int64_t lda, float* sa,
                             float* sc, int64_t ldsc, int64_t M, int64_t N,
                             int64_t K, void* workspace,
                             size_t workspace_bytes, void* stream);
+/*
+ * Block-scaled FP8 GEMM with one scale per row and 128-K group on both
+ * operands:  C[m][n] = sum_kb sa(m,kb) * sb(n,kb) * P(m,n,kb), P the FP8 x FP8
+ * dot product of group kb accumulated in FP32, promoted with one FP32
+ * multiply-add per group.  This is the weight-gradient GEMM
+ * dW[N][K] = dY^T . X: a = dY^T and b = X^T from fp8_quant_act_128x1_t,
+ * the GEMM's K being the token count.
+ * Pages: "Advantages of using FP8 for GEMM operations in DeepSeek-V3",
+ * items 1 and 5 (FP8 GEMMs with FP32 promotion at fixed intervals); "How
+ * the unified E4M3 format adds to DeepSeek-V3's efficiency", section
+ * "Fine-grained quantization strategy" (the same format in the backward
+ * pass).
+ *
+ *   a, sa   E4M3 codes [M][lda], sa(m,kb) at sa[kb*ldsa + m], ldsa >= M.
+ *   b, sb   E4M3 codes [N][ldb], sb(n,kb) at sb[kb*ldsb + n], ldsb >= N.
+ *   c       [M][ldc], fp32 or bf16 by out_kind.
+ * Errors: as fp8_block_gemm.
+ */
+int fp8_block_gemm_rowscaled(const uint8_t* a, int64_t lda, const float* sa,
+                             int64_t ldsa, const uint8_t* b, int64_t ldb,
+                             const float* sb, int64_t ldsb, void* c,
+                             int64_t ldc, int out_kind, int64_t M, int64_t N,
+                             int64_t K, void* stream);
 /*
  * Grouped (MoE) block-scaled FP8 GEMM: rows group_offsets[g] ..
  * group_offsets[g+1]-1 of A are multiplied by expert g's weight.

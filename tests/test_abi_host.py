@@ -196,6 +196,45 @@ def test_delayed_validation(fp8bs):
     assert d(hist=P + 2) == fp8bs.ERR_LAYOUT
 
 
+def test_backward_calls_validation(fp8bs):
+    lib = fp8bs.lib
+
+    def wt(w=P, N=256, K=256, ldw=256, q=P, ldq=256, s=P, qt=P, ldqt=256, st=P):
+        return lib.fp8_quant_w_128x128_t(w, N, K, ldw, q, ldq, s, qt, ldqt, st, None)
+
+    assert wt(N=200) == fp8bs.ERR_SHAPE  # transposed rows need whole 128-column groups
+    assert wt(K=100) == fp8bs.ERR_SHAPE
+    assert wt(N=0) == fp8bs.OK
+    assert wt(qt=0) == fp8bs.ERR_NULL
+    assert wt(st=0) == fp8bs.ERR_NULL
+    assert wt(ldqt=255) == fp8bs.ERR_LAYOUT
+    assert wt(qt=P + 8) == fp8bs.ERR_LAYOUT
+
+    def at(x=P, M=256, N=256, ldx=256, qt=P, ldqt=256, st=P, ldst=256):
+        return lib.fp8_quant_act_128x1_t(x, M, N, ldx, qt, ldqt, st, ldst, None)
+
+    assert at(M=200) == fp8bs.ERR_SHAPE
+    assert at(N=100) == fp8bs.ERR_SHAPE
+    assert at(M=0) == fp8bs.OK
+    assert at(x=0) == fp8bs.ERR_NULL
+    assert at(ldqt=128) == fp8bs.ERR_LAYOUT
+    assert at(ldst=255) == fp8bs.ERR_LAYOUT
+    assert at(x=P + 4) == fp8bs.ERR_LAYOUT
+
+    def rs(a=P, lda=256, sa=P, ldsa=64, b=P, ldb=256, sb=P, ldsb=128, c=P, ldc=128, out_kind=0,
+           M=64, N=128, K=256):
+        return lib.fp8_block_gemm_rowscaled(a, lda, sa, ldsa, b, ldb, sb, ldsb, c, ldc, out_kind,
+                                            M, N, K, None)
+
+    assert rs(out_kind=2) == fp8bs.ERR_DTYPE
+    assert rs(K=130) == fp8bs.ERR_SHAPE
+    assert rs(M=0) == fp8bs.OK
+    assert rs(sb=0) == fp8bs.ERR_NULL
+    assert rs(ldsb=127) == fp8bs.ERR_LAYOUT
+    assert rs(ldsa=63) == fp8bs.ERR_LAYOUT
+    assert rs(b=P + 8) == fp8bs.ERR_LAYOUT
+
+
 def test_workspace_query(fp8bs):
     lib = fp8bs.lib
     assert lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_E4M3, 64, 128, 256, 0) == 0

@@ -1,0 +1,177 @@
+"""GPU parity of the backward-pass pieces against the oracle: the transposed
+weight quantizer and the 128-token quantizer (bit-exact), the GEMM with
+per-row scales on both operands, and the data and weight gradients end to
+end (GPU quantizers, then GPU GEMMs, against the oracle on the same bf16
+inputs)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_05_amd import synth
+from tests import _gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp8bs():
+    from fp8_block_scaled_05_amd import fp8bs as mod
+    return mod
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (256, 384), (384, 1024)])
+def test_weight_quantizer_transposed_bit_exact(fp8bs, N, K):
+    w = synth.weight(N, K, case=800 + N, tensor=1)
+    q, s, qt, st = fp8bs.fp8_quant_w_128x128_t(w.cuda())
+    torch.cuda.synchronize()
+    q_o, s_o, qt_o, st_o = oracle.quant_w_128x128_t(synth.bf16_bits(w))
+    gu.assert_same_bits(gu.host(q), q_o, "codes")
+    gu.assert_same_bits(gu.host(s), s_o, "scales")
+    gu.assert_same_bits(gu.host(qt), qt_o, "transposed codes")
+    gu.assert_same_bits(gu.host(st), st_o, "transposed scales")
+
+
+@pytest.mark.parametrize("M,N", [(128, 128), (256, 384), (640, 256)])
+def test_token_group_quantizer_bit_exact(fp8bs, M, N):
+    x = synth.act(M, N, case=810 + M, tensor=0)
+    qt, st = fp8bs.fp8_quant_act_128x1_t(x.cuda())
+    torch.cuda.synchronize()
+    qt_o, st_o = oracle.quant_act_128x1_t(synth.bf16_bits(x))
+    gu.assert_same_bits(gu.host(qt), qt_o, "codes")
+    gu.assert_same_bits(gu.host(st), st_o, "scales")
+
+
+def test_token_group_quantizer_strided(fp8bs):
+    M, N = 256, 256
+    X = synth.act(M, N + 64, case=815, tensor=0).cuda()
+    QT = torch.full((N, M + 32), 0x33, dtype=torch.uint8, device="cuda")
+    ST = torch.full((M // 128, N + 8), -1.0, dtype=torch.float32, device="cuda")
+    fp8bs.fp8_quant_act_128x1_t(X[:, :N], qt=QT[:, :M], st=ST)
+    torch.cuda.synchronize()
+    qt_o, st_o = oracle.quant_act_128x1_t(synth.bf16_bits(X[:, :N]))
+    gu.assert_same_bits(gu.host(QT[:, :M]), qt_o, "codes")
+    gu.assert_same_bits(gu.host(ST[:, :N]), st_o, "scales")
+    assert torch.all(QT[:, M:] == 0x33) and torch.all(ST[:, N:] == -1.0)
+
+
+@pytest.mark.parametrize("M,N,K,out", [
+    (300, 384, 512, torch.float32),   # 256x256 tiles, ragged M
+    (257, 200, 256, torch.bfloat16),  # ragged N
+    (48, 256, 384, torch.float32),    # few-row tile
+    (20, 72, 256, torch.float32),     # 32x32 tile, ragged
+])
+def test_rowscaled_gemm(fp8bs, M, N, K, out):
+    a = synth.act(M, K, case=820 + M, tensor=0)
+    b = synth.act(N, K, case=820 + M, tensor=1)
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(a))
+    qb, sb = oracle.quant_act_1x128(synth.bf16_bits(b))
+    c = fp8bs.fp8_block_gemm_rowscaled(gu.u8(qa), gu.f32(sa), gu.u8(qb), gu.f32(sb),
+                                       out_dtype=out)
+    torch.cuda.synchronize()
+    C, B = oracle.block_gemm_rowscaled(qa, sa, qb, sb)
+    gu.check_gemm(c, C, B)
+
+
+def test_rowscaled_gemm_adversarial_scales(fp8bs):
+    """Per-row, per-group scales spanning 2^+-20 on both operands: a kernel
+    that applied either scale outside the per-group promotion, or to the
+    wrong row or column, would fail the tolerance."""
+    M, N, K = 130, 260, 1024
+    rng = np.random.default_rng(21)
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(synth.act(M, K, case=830, tensor=0)))
+    qb, sb = oracle.quant_act_1x128(synth.bf16_bits(synth.act(N, K, case=830, tensor=1)))
+    sa = (sa * np.float32(2.0) ** rng.integers(-20, 21, sa.shape)).astype(np.float32)
+    sb = (sb * np.float32(2.0) ** rng.integers(-20, 21, sb.shape)).astype(np.float32)
+    c = fp8bs.fp8_block_gemm_rowscaled(gu.u8(qa), gu.f32(sa), gu.u8(qb), gu.f32(sb))
+    torch.cuda.synchronize()
+    C, B = oracle.block_gemm_rowscaled(qa, sa, qb, sb)
+    gu.check_gemm(c, C, B)
+
+
+def test_rowscaled_gemm_last_round_split(fp8bs):
+    """272 tiles (> 256 compute units, not whole rounds): the last partial
+    round runs as half-height tiles with row-scaled B as well."""
+    M, N, K = 4352, 4096, 128
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(synth.act(M, K, case=835, tensor=0)))
+    qb, sb = oracle.quant_act_1x128(synth.bf16_bits(synth.act(N, K, case=835, tensor=1)))
+    c = fp8bs.fp8_block_gemm_rowscaled(gu.u8(qa), gu.f32(sa), gu.u8(qb), gu.f32(sb))
+    torch.cuda.synchronize()
+    C, B = oracle.block_gemm_rowscaled(qa, sa, qb, sb)
+    gu.check_gemm(c, C, B)
+
+
+def test_data_gradient_end_to_end(fp8bs):
+    """dX = dY . W: dY quantized per 1x128 along N, W per 128x128 block read
+    transposed; every output against the oracle."""
+    M, N, K = 300, 384, 256
+    dy = synth.act(M, N, case=840, tensor=0)
+    w = synth.weight(N, K, case=840, tensor=1)
+    qdy, sdy = fp8bs.fp8_quant_act_1x128(dy.cuda())
+    _, _, qt, st = fp8bs.fp8_quant_w_128x128_t(w.cuda())
+    dx = fp8bs.fp8_block_gemm(qdy, sdy, qt, st, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qdy_o, sdy_o, qt_o, st_o, C, B = oracle.dgrad(synth.bf16_bits(dy), synth.bf16_bits(w))
+    gu.assert_same_bits(gu.host(qdy), qdy_o, "dY codes")
+    gu.assert_same_bits(gu.host(qt), qt_o, "W^T codes")
+    gu.check_gemm(dx, C, B)
+
+
+def test_weight_gradient_end_to_end(fp8bs):
+    """dW = dY^T . X: both quantized in 128-token groups; every output
+    against the oracle."""
+    M, N, K = 384, 256, 384
+    dy = synth.act(M, N, case=850, tensor=0)
+    x = synth.act(M, K, case=850, tensor=1)
+    qdyt, sdyt = fp8bs.fp8_quant_act_128x1_t(dy.cuda())
+    qxt, sxt = fp8bs.fp8_quant_act_128x1_t(x.cuda())
+    dw = fp8bs.fp8_block_gemm_rowscaled(qdyt, sdyt, qxt, sxt)
+    torch.cuda.synchronize()
+    qdyt_o, _, qxt_o, _, C, B = oracle.wgrad(synth.bf16_bits(dy), synth.bf16_bits(x))
+    gu.assert_same_bits(gu.host(qdyt), qdyt_o, "dY^T codes")
+    gu.assert_same_bits(gu.host(qxt), qxt_o, "X^T codes")
+    gu.check_gemm(dw, C, B)
+
+
+def test_full_size_gradients_sampled(fp8bs):
+    """Backward of the dense layer at full size (tokens M=4096, N=18432,
+    K=7168): dX [4096][7168] (contraction 18432, bf16) and dW [18432][7168]
+    (contraction 4096, fp32).  Sampled rows x sampled 128-column blocks
+    against the oracle, which needs only those columns of W and X."""
+    M, N, K = 4096, 18432, 7168
+    dy = synth.act(M, N, case=synth.DENSE.case_id, tensor=20, device="cuda")
+    w = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
+    x = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
+    qdy, sdy = fp8bs.fp8_quant_act_1x128(dy)
+    _, _, qt, st = fp8bs.fp8_quant_w_128x128_t(w)
+    dx = fp8bs.fp8_block_gemm(qdy, sdy, qt, st, out_dtype=torch.bfloat16)
+    qdyt, sdyt = fp8bs.fp8_quant_act_128x1_t(dy)
+    qxt, sxt = fp8bs.fp8_quant_act_128x1_t(x)
+    dw = fp8bs.fp8_block_gemm_rowscaled(qdyt, sdyt, qxt, sxt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    kbs = sorted(set([0, K // 128 - 1] + rng.choice(K // 128, 2, replace=False).tolist()))
+    dy_bits = synth.bf16_bits(dy)
+    w_bits = synth.bf16_bits(w)
+    x_bits = synth.bf16_bits(x)
+    dx_h, dw_h = gu.host_f64(dx), gu.host_f64(dw)
+    qt_h, qxt_h = gu.host(qt), gu.host(qxt)
+    # data gradient: sampled rows of dY, all N, output column blocks kb
+    rows = np.array(sorted(set([0, M - 1] + rng.choice(M, 4, replace=False).tolist())))
+    qd, sd = oracle.quant_act_1x128(dy_bits[rows])
+    gu.assert_same_bits(gu.host(qdy)[rows], qd, "sampled dY codes")
+    # weight gradient: sampled rows n of dW (columns of dY), all tokens
+    ns = np.array(sorted(set([0, N - 1] + rng.choice(N, 4, replace=False).tolist())))
+    qa_o, sa_o = oracle.quant_act_128x1_t(dy_bits[:, ns])
+    gu.assert_same_bits(gu.host(qdyt)[ns], qa_o, "sampled dY^T codes")
+    for kb in kbs:
+        cols = slice(kb * 128, (kb + 1) * 128)
+        _, _, qt_o, st_o = oracle.quant_w_128x128_t(w_bits[:, cols])
+        gu.assert_same_bits(qt_h[cols], qt_o, f"W^T codes, block {kb}")
+        C, B = oracle.block_gemm(qd, sd, qt_o, st_o)
+        gu.check_gemm(dx_h[rows][:, cols], C, B, bf16=True)
+        qb_o, sb_o = oracle.quant_act_128x1_t(x_bits[:, cols])
+        gu.assert_same_bits(qxt_h[cols], qb_o, f"X^T codes, block {kb}")
+        C2, B2 = oracle.block_gemm_rowscaled(qa_o, sa_o, qb_o, sb_o)
+        gu.check_gemm(dw_h[ns][:, cols], C2, B2)
