@@ -13,7 +13,8 @@ path: the activation and weight quantizers alone at 8192x7168 / 18432x7168
 (32 experts, top-8 of 4096 tokens, gate/up and down), the skinny GEMM with
 in-call activation quantization (M = 16, 64), the dense GEMM with its output
 quantized for the next FP8 GEMM (against bf16 output followed by the
-activation quantizer), online against delayed (history-based) scaling on a
+activation quantizer), the backward pass of the dense layer (data and weight
+gradients with their quantizers), online against delayed (history-based) scaling on a
 drifting sequence of activations (quantization error, clipped and flushed
 fractions), and the CPU oracle on a bounded sample of the dense step
 (``cpu_baseline``).
@@ -245,6 +246,53 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         "gemms_TFLOPs": (f1 + f2) / (g1 + g2) / 1e9,
         "gemms_frac_mfma": (f1 + f2) / (g1 + g2) / 1e9 / PEAK_FP8_TFLOPS,
         "step_with_quant_us": tot * 1e3, "step_TFLOPs": (f1 + f2) / tot / 1e9}
+
+    # backward pass of the dense layer (tokens 4096, N=18432, K=7168):
+    # quantizers with transposed outputs, data gradient dX = dY . W
+    # (contraction 18432) and weight gradient dW = dY^T . X (contraction 4096)
+    Mb = M
+    dy = synth.act(Mb, N, case=synth.DENSE.case_id, tensor=20, device="cuda")
+    xb = synth.act(Mb, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
+    wb = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
+    bq = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    bs = torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda")
+    bqt = torch.empty(K, N, dtype=torch.uint8, device="cuda")
+    bst = torch.empty(K // 128, N // 128, dtype=torch.float32, device="cuda")
+    qdy = torch.empty(Mb, N, dtype=torch.uint8, device="cuda")
+    sdy = torch.empty(N // 128, Mb, dtype=torch.float32, device="cuda")
+    qdyt = torch.empty(N, Mb, dtype=torch.uint8, device="cuda")
+    sdyt = torch.empty(Mb // 128, N, dtype=torch.float32, device="cuda")
+    qxt = torch.empty(K, Mb, dtype=torch.uint8, device="cuda")
+    sxt = torch.empty(Mb // 128, K, dtype=torch.float32, device="cuda")
+    dx = torch.empty(Mb, K, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
+
+    def bwd(timed):
+        run = tm.run if timed else (lambda n, f: f())
+        run("b_qw", lambda: fp8bs.fp8_quant_w_128x128_t(wb, bq, bs, bqt, bst))
+        run("b_qdy", lambda: fp8bs.fp8_quant_act_1x128(dy, qdy, sdy))
+        run("b_qdyt", lambda: fp8bs.fp8_quant_act_128x1_t(dy, qdyt, sdyt))
+        run("b_qxt", lambda: fp8bs.fp8_quant_act_128x1_t(xb, qxt, sxt))
+        run("b_dx", lambda: fp8bs.fp8_block_gemm(qdy, sdy, bqt, bst, out=dx))
+        run("b_dw", lambda: fp8bs.fp8_block_gemm_rowscaled(qdyt, sdyt, qxt, sxt, out=dw))
+
+    for i in range(iters + 5):
+        bwd(i >= 5)
+    fl = 2.0 * Mb * N * K
+    t = {k: tm.avg_ms(k) for k in ("b_qw", "b_qdy", "b_qdyt", "b_qxt", "b_dx", "b_dw")}
+    out["backward_dense_M4096_N18432_K7168"] = {
+        "weight_quant_with_transpose_us": t["b_qw"] * 1e3,
+        "weight_quant_with_transpose_GBps": N * K * 4 / t["b_qw"] / 1e6,
+        "dy_quant_1x128_us": t["b_qdy"] * 1e3,
+        "dy_quant_128x1_t_us": t["b_qdyt"] * 1e3,
+        "dy_quant_128x1_t_GBps": Mb * N * 3.03125 / t["b_qdyt"] / 1e6,
+        "x_quant_128x1_t_us": t["b_qxt"] * 1e3,
+        "dgrad_us": t["b_dx"] * 1e3, "dgrad_TFLOPs": fl / t["b_dx"] / 1e9,
+        "dgrad_frac_mfma": fl / t["b_dx"] / 1e9 / PEAK_FP8_TFLOPS,
+        "wgrad_us": t["b_dw"] * 1e3, "wgrad_TFLOPs": fl / t["b_dw"] / 1e9,
+        "wgrad_frac_mfma": fl / t["b_dw"] / 1e9 / PEAK_FP8_TFLOPS,
+        "step_us": sum(t.values()) * 1e3}
+    del dy, xb, wb, bq, bs, bqt, bst, qdy, sdy, qdyt, sdyt, qxt, sxt, dx, dw
 
     # online vs delayed scaling on drifting activations (quality, not speed)
     from fp8_block_scaled_05_amd import ablation
