@@ -175,3 +175,56 @@ def test_full_size_gradients_sampled(fp8bs):
         gu.assert_same_bits(qxt_h[cols], qb_o, f"X^T codes, block {kb}")
         C2, B2 = oracle.block_gemm_rowscaled(qa_o, sa_o, qb_o, sb_o)
         gu.check_gemm(dw_h[ns][:, cols], C2, B2)
+
+
+def test_moe_data_gradient_grouped(fp8bs):
+    """MoE data gradient dX_g = dY_g . W_g with the grouped GEMM: each
+    expert's weight quantized with its transposed copy; the stacked
+    [G][K][N] codes and [G][K/128][N/128] scales are the grouped call's
+    expert layout.  Every output against the oracle, expert by expert."""
+    sizes = [70, 0, 300, 129, 5]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    G, M, N, K = len(sizes), int(offsets[-1]), 256, 384
+    dy = synth.act(M, N, case=860, tensor=0)
+    ws = [synth.weight(N, K, case=860, tensor=10 + g) for g in range(G)]
+    qt = torch.empty(G, K, N, dtype=torch.uint8, device="cuda")
+    st = torch.empty(G, K // 128, N // 128, dtype=torch.float32, device="cuda")
+    for g in range(G):
+        fp8bs.fp8_quant_w_128x128_t(ws[g].cuda(), qt=qt[g], st=st[g])
+    qdy, sdy = fp8bs.fp8_quant_act_1x128(dy.cuda())
+    dx = fp8bs.fp8_block_grouped_gemm(qdy, sdy, qt, st, torch.from_numpy(offsets).cuda(),
+                                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    dx_h = gu.host_f64(dx)
+    for g, (r0, r1) in enumerate(zip(offsets[:-1], offsets[1:])):
+        if r1 == r0:
+            continue
+        _, _, qt_o, st_o, C, B = oracle.dgrad(synth.bf16_bits(dy[r0:r1]), synth.bf16_bits(ws[g]))
+        gu.assert_same_bits(gu.host(qt[g]), qt_o, f"expert {g} W^T codes")
+        gu.check_gemm(dx_h[r0:r1], C, B)
+
+
+def test_moe_weight_gradient_per_expert(fp8bs):
+    """MoE weight gradient dW_g = dY_g^T . X_g over each expert's tokens,
+    padded with zero rows to a multiple of 128 (zeros change neither the
+    group maxima nor the sums): the padded oracle equals the unpadded
+    definition, and the GPU matches it."""
+    sizes = [70, 300, 129]
+    N, K = 128, 256
+    rng_case = 870
+    for g, mg in enumerate(sizes):
+        dy = synth.act(mg, N, case=rng_case, tensor=g)
+        x = synth.act(mg, K, case=rng_case, tensor=100 + g)
+        mp = (mg + 127) // 128 * 128
+        dyp = torch.zeros(mp, N, dtype=torch.bfloat16)
+        xp = torch.zeros(mp, K, dtype=torch.bfloat16)
+        dyp[:mg] = dy
+        xp[:mg] = x
+        qa, sa = fp8bs.fp8_quant_act_128x1_t(dyp.cuda())
+        qb, sb = fp8bs.fp8_quant_act_128x1_t(xp.cuda())
+        dw = fp8bs.fp8_block_gemm_rowscaled(qa, sa, qb, sb)
+        torch.cuda.synchronize()
+        qa_o, sa_o, qb_o, sb_o, C, B = oracle.wgrad(synth.bf16_bits(dyp), synth.bf16_bits(xp))
+        gu.assert_same_bits(gu.host(qa), qa_o, f"expert {g} dY^T codes")
+        gu.assert_same_bits(gu.host(qb), qb_o, f"expert {g} X^T codes")
+        gu.check_gemm(dw, C, B)

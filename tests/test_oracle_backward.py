@@ -117,3 +117,27 @@ def test_weight_gradient_closed_form():
     qdyt, sdyt, qxt, sxt, C, _ = oracle.wgrad(_bits(dy), _bits(x))
     assert np.all(sdyt == 1.0) and np.all(sxt == 1.0)
     assert np.array_equal(C, dy.T @ x)
+
+
+def test_zero_token_padding_changes_nothing():
+    """Padding a ragged token count with zero rows to a multiple of 128 gives
+    the same weight gradient (zeros raise no maximum and add nothing) as
+    long as the real tokens fill the first groups; here the last group is
+    part real, part padding."""
+    rng = np.random.default_rng(7)
+    mg, N, K = 200, 16, 24
+    dy = rng.standard_normal((mg, N))
+    x = rng.standard_normal((mg, K))
+    dyp = np.zeros((256, N))
+    xp = np.zeros((256, K))
+    dyp[:mg] = dy
+    xp[:mg] = x
+    _, sa, _, sb, C, _ = oracle.wgrad(_bits(dyp), _bits(xp))
+    # group 1 holds tokens 128..199 and zeros: its maxima are those of the real tokens
+    xf = _f32(_bits(dyp))
+    assert np.array_equal(sa[1], np.divide(np.max(np.abs(xf[128:mg]), axis=0).astype(np.float32),
+                                           np.float32(448.0), dtype=np.float32))
+    # and the gradient equals the sum over the two groups computed from the real tokens only
+    a = oracle.decode(oracle.quant_act_128x1_t(_bits(dyp))[0]).T * np.repeat(sa, 128, axis=0)
+    b = oracle.decode(oracle.quant_act_128x1_t(_bits(xp))[0]).T * np.repeat(sb, 128, axis=0)
+    assert np.allclose(C, a[:mg].T @ b[:mg], rtol=1e-12, atol=0)
