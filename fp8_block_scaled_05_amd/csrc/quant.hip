@@ -216,7 +216,9 @@ __global__ __launch_bounds__(256) void quant_act_128x1_t_kernel(
     *reinterpret_cast<u32x2*>(tile + (r0 + 16 * i) * kPitch + lane * 8) = u32x2{lo, hi};
   }
   __syncthreads();
-  const int c0 = (threadIdx.x & 15) * 8, m0 = (threadIdx.x >> 4) * 8;
+  // 16 consecutive threads cover the 128 tokens of one output row (whole
+  // 128-byte lines per store)
+  const int m0 = (threadIdx.x & 15) * 8, c0 = (threadIdx.x >> 4) * 8;
   uint32_t lo[8], hi[8], olo[8], ohi[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
