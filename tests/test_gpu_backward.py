@@ -74,6 +74,45 @@ def test_rowscaled_gemm(fp8bs, M, N, K, out):
     gu.check_gemm(c, C, B)
 
 
+def test_rowscaled_gemm_strided(fp8bs):
+    """Operands and scales inside wider buffers (lda, ldb > K; ldsa > M,
+    ldsb > N; ldc > N): the padding is neither read into the result nor
+    written."""
+    M, N, K = 130, 200, 384
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(synth.act(M, K, case=825, tensor=0)))
+    qb, sb = oracle.quant_act_1x128(synth.bf16_bits(synth.act(N, K, case=825, tensor=1)))
+    A = torch.full((M, K + 32), 0x7E, dtype=torch.uint8, device="cuda")
+    B = torch.full((N, K + 48), 0x7E, dtype=torch.uint8, device="cuda")
+    SA = torch.full((K // 128, M + 6), 1e30, dtype=torch.float32, device="cuda")
+    SB = torch.full((K // 128, N + 10), 1e30, dtype=torch.float32, device="cuda")
+    A[:, :K] = gu.u8(qa)
+    B[:, :K] = gu.u8(qb)
+    SA[:, :M] = gu.f32(sa)
+    SB[:, :N] = gu.f32(sb)
+    C = torch.full((M, N + 16), -3.0, dtype=torch.float32, device="cuda")
+    fp8bs.fp8_block_gemm_rowscaled(A[:, :K], SA, B[:, :K], SB, out=C[:, :N])
+    torch.cuda.synchronize()
+    Cr, Br = oracle.block_gemm_rowscaled(qa, sa, qb, sb)
+    gu.check_gemm(C[:, :N], Cr, Br)
+    assert torch.all(C[:, N:] == -3.0)
+
+
+def test_weight_quantizer_transposed_strided(fp8bs):
+    N, K = 256, 384
+    w = synth.weight(N, K + 64, case=805, tensor=1).cuda()
+    Q = torch.full((N, K + 16), 0x11, dtype=torch.uint8, device="cuda")
+    QT = torch.full((K, N + 32), 0x22, dtype=torch.uint8, device="cuda")
+    s = torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda")
+    st = torch.empty(K // 128, N // 128, dtype=torch.float32, device="cuda")
+    fp8bs.fp8_quant_w_128x128_t(w[:, :K], q=Q[:, :K], s=s, qt=QT[:, :N], st=st)
+    torch.cuda.synchronize()
+    q_o, s_o, qt_o, st_o = oracle.quant_w_128x128_t(synth.bf16_bits(w[:, :K]))
+    gu.assert_same_bits(gu.host(Q[:, :K]), q_o, "codes")
+    gu.assert_same_bits(gu.host(QT[:, :N]), qt_o, "transposed codes")
+    gu.assert_same_bits(gu.host(st), st_o, "transposed scales")
+    assert torch.all(Q[:, K:] == 0x11) and torch.all(QT[:, N:] == 0x22)
+
+
 def test_rowscaled_gemm_adversarial_scales(fp8bs):
     """Per-row, per-group scales spanning 2^+-20 on both operands: a kernel
     that applied either scale outside the per-group promotion, or to the

@@ -241,3 +241,25 @@ def test_full_size_dense_sampled(fp8bs):
         worst = max(worst, check_e4m3_out(qc_h[:, nb * 128:(nb + 1) * 128], sc_h[nb:nb + 1],
                                           C, B, C_codes=qc_ref))
     print(f"e4m3-out full-size sampled: worst err/bound = {worst:.4f}")
+
+
+def test_grouped_many_groups(fp8bs):
+    """More groups than a wave scans at once (G = 100), many of them empty or
+    tiny, with quantized output."""
+    rng = np.random.default_rng(31)
+    sizes = rng.integers(0, 5, 100)
+    sizes[rng.choice(100, 3, replace=False)] = [200, 129, 64]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, N, K = int(offsets[-1]), 128, 256
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(synth.act(M, K, case=650, tensor=0)))
+    qw, sw = _experts(len(sizes), N, K, 650)
+    qc, sc = fp8bs.fp8_block_grouped_gemm_e4m3_out(
+        gu.u8(qa), gu.f32(sa), gu.u8(qw), gu.f32(sw), torch.from_numpy(offsets).cuda())
+    torch.cuda.synchronize()
+    qc_h, sc_h = gu.host(qc), gu.host(sc)
+    for g, (r0, r1) in enumerate(zip(offsets[:-1], offsets[1:])):
+        if r1 == r0:
+            continue
+        C, B, qc_ref, _ = oracle.block_gemm_e4m3_out(qa[r0:r1], sa[:, r0:r1], qw[g], sw[g])
+        check_e4m3_out(qc_h[r0:r1], sc_h[:, r0:r1], C, B, C_codes=qc_ref,
+                       min_equal=0.99 if r1 - r0 > 20 else 0.9)
