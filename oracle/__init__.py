@@ -47,6 +47,7 @@ from .quant import (  # noqa: F401
 from .backward import (  # noqa: F401
     block_gemm_rowscaled,
     dgrad,
+    kgrouped_gemm_rowscaled,
     quant_act_128x1_t,
     quant_w_128x128_t,
     wgrad,

@@ -97,3 +97,27 @@ def wgrad(dy_bits, x_bits):
     qxt, sxt = quant_act_128x1_t(x_bits)
     C, B = block_gemm_rowscaled(qdyt, sdyt, qxt, sxt)
     return qdyt, sdyt, qxt, sxt, C, B
+
+
+def kgrouped_gemm_rowscaled(qa, sa, qb, sb, offsets):
+    """MoE weight gradients in one call: for every expert g,
+    C[g] = A[:, t0:t1] . B[:, t0:t1]^T over its token columns
+    [t0, t1) = [offsets[g], offsets[g+1]) (multiples of 128: each expert's
+    tokens padded with zero rows), with per-row scales on both operands as
+    ``block_gemm_rowscaled``.  qa [M][T], sa [T/128][M]; qb [N][T],
+    sb [T/128][N].  An expert without tokens gets C[g] = 0.
+    Returns ``(C, B)`` float64 [G][M][N].
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    assert np.all(offsets % TILE == 0)
+    G = len(offsets) - 1
+    M, N = qa.shape[0], qb.shape[0]
+    C = np.zeros((G, M, N))
+    B = np.zeros((G, M, N))
+    for g in range(G):
+        t0, t1 = int(offsets[g]), int(offsets[g + 1])
+        if t1 == t0:
+            continue
+        C[g], B[g] = block_gemm_rowscaled(qa[:, t0:t1], np.asarray(sa)[t0 // TILE:t1 // TILE],
+                                          qb[:, t0:t1], np.asarray(sb)[t0 // TILE:t1 // TILE])
+    return C, B

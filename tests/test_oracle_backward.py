@@ -141,3 +141,25 @@ def test_zero_token_padding_changes_nothing():
     a = oracle.decode(oracle.quant_act_128x1_t(_bits(dyp))[0]).T * np.repeat(sa, 128, axis=0)
     b = oracle.decode(oracle.quant_act_128x1_t(_bits(xp))[0]).T * np.repeat(sb, 128, axis=0)
     assert np.allclose(C, a[:mg].T @ b[:mg], rtol=1e-12, atol=0)
+
+
+def test_kgrouped_equals_per_expert_and_zero_for_empty():
+    """The one-call MoE weight gradient is the row-scaled GEMM of each
+    expert's token columns (checked against slices computed directly from
+    the dequantized operands), and zero for an expert without tokens."""
+    rng = np.random.default_rng(8)
+    sizes = [256, 0, 128, 384]
+    offsets = np.concatenate([[0], np.cumsum(sizes)])
+    T, M, N = int(offsets[-1]), 24, 40
+    dy = _bits(rng.standard_normal((T, M)))
+    x = _bits(rng.standard_normal((T, N)))
+    qa, sa = oracle.quant_act_128x1_t(dy)
+    qb, sb = oracle.quant_act_128x1_t(x)
+    C, B = oracle.kgrouped_gemm_rowscaled(qa, sa, qb, sb, offsets)
+    a = oracle.decode(qa) * np.repeat(sa.T.astype(np.float64), 128, axis=1)
+    b = oracle.decode(qb) * np.repeat(sb.T.astype(np.float64), 128, axis=1)
+    for g in range(4):
+        t0, t1 = offsets[g], offsets[g + 1]
+        want = a[:, t0:t1] @ b[:, t0:t1].T
+        assert np.all(np.abs(C[g] - want) <= 1e-12 * np.maximum(B[g], 1e-300))
+    assert not C[1].any() and not B[1].any()
