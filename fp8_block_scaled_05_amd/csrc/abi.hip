@@ -260,6 +260,45 @@ int fp8_block_gemm_rowscaled(const uint8_t* a, int64_t lda, const float* sa, int
                                                        static_cast<hipStream_t>(stream)));
 }
 
+int fp8_block_kgrouped_gemm_rowscaled(const uint8_t* a, int64_t lda, const float* sa,
+                                      int64_t ldsa, const uint8_t* b, int64_t ldb,
+                                      const float* sb, int64_t ldsb, void* c, int64_t ldc,
+                                      int64_t c_group_stride, int out_kind,
+                                      const int32_t* group_offsets, int64_t G, int64_t M,
+                                      int64_t N, int64_t K_total, void* stream) {
+  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+  if (G < 1 || G > kMaxGroups || M < 0 || N < 0 || K_total < 0 || K_total % kTile != 0)
+    return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!a || !sa || !b || !sb || !c || !group_offsets) return FP8BS_ERR_NULL;
+  if (!ld_ok(lda, K_total) || !ld_ok(ldb, K_total) || ldc < N || ldsa < M || ldsb < N ||
+      c_group_stride < (M - 1) * ldc + N)
+    return FP8BS_ERR_LAYOUT;
+  const uintptr_t c_align = out_kind == FP8BS_OUT_F32 ? 4 : 2;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sa, 4) ||
+      !aligned(sb, 4) || !aligned(group_offsets, 4))
+    return FP8BS_ERR_LAYOUT;
+  fp8bs::GemmArgs g{};
+  g.a = a;
+  g.lda = lda;
+  g.sa = sa;
+  g.ldsa = ldsa;
+  g.b = b;
+  g.ldb = ldb;
+  g.sb = sb;
+  g.sb_ld = ldsb;
+  g.c = c;
+  g.ldc = ldc;
+  g.c_group_stride = c_group_stride;
+  g.M = M;
+  g.N = N;
+  g.K = K_total;
+  g.group_offsets = group_offsets;
+  g.G = G;
+  return hip_status(fp8bs::launch_kgrouped_gemm_rowscaled(g, out_of(out_kind),
+                                                          static_cast<hipStream_t>(stream)));
+}
+
 int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                            const uint8_t* b, int64_t ldb, int64_t b_group_stride,
                            const float* sb, void* c, int64_t ldc, int out_kind,

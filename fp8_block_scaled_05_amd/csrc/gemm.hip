@@ -33,20 +33,27 @@ using Rows64Cfg = gemm::Cfg<64, 128, 1, 4, 4, 1>;
 hipError_t launch_block_gemm(const GemmArgs& args, OutKind out, hipStream_t stream) {
   // E4M3 output quantizes whole 128-column tiles inside a workgroup: the
   // 32-column few-row tile cannot, so E4M3 output uses the 64x128 tile
-  if (args.M <= 32 && out != kOutE4M3) return gemm::launch<Rows32Cfg, false>(args, out, stream);
-  if (args.M <= 64) return gemm::launch<Rows64Cfg, false>(args, out, stream);
-  return gemm::launch<LargeCfg, false, LargeTail>(args, out, stream);
+  if (args.M <= 32 && out != kOutE4M3) return gemm::launch<Rows32Cfg, gemm::kDense>(args, out, stream);
+  if (args.M <= 64) return gemm::launch<Rows64Cfg, gemm::kDense>(args, out, stream);
+  return gemm::launch<LargeCfg, gemm::kDense, LargeTail>(args, out, stream);
 }
 
 hipError_t launch_block_gemm_rowscaled(const GemmArgs& args, OutKind out, hipStream_t stream) {
   using gemm::RowScaledB;
-  if (args.M <= 32) return gemm::launch<RowScaledB<Rows32Cfg>, false>(args, out, stream);
-  if (args.M <= 64) return gemm::launch<RowScaledB<Rows64Cfg>, false>(args, out, stream);
-  return gemm::launch<RowScaledB<LargeCfg>, false, RowScaledB<LargeTail>>(args, out, stream);
+  if (args.M <= 32) return gemm::launch<RowScaledB<Rows32Cfg>, gemm::kDense>(args, out, stream);
+  if (args.M <= 64) return gemm::launch<RowScaledB<Rows64Cfg>, gemm::kDense>(args, out, stream);
+  return gemm::launch<RowScaledB<LargeCfg>, gemm::kDense, RowScaledB<LargeTail>>(args, out, stream);
+}
+
+hipError_t launch_kgrouped_gemm_rowscaled(const GemmArgs& args, OutKind out,
+                                          hipStream_t stream) {
+  using gemm::RowScaledB;
+  return gemm::launch<RowScaledB<LargeCfg>, gemm::kGroupK, RowScaledB<LargeTail>>(args, out,
+                                                                                   stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, OutKind out, hipStream_t stream) {
-  return gemm::launch<LargeCfg, true, LargeTail>(args, out, stream);
+  return gemm::launch<LargeCfg, gemm::kGroupRows, LargeTail>(args, out, stream);
 }
 
 }  // namespace fp8bs

@@ -12,17 +12,24 @@
 // interval is the 128-K group, where the scales change.
 //
 // Structure: WM x WN waves per BM x BN output tile; each wave owns a
-// (BM/WM) x (BN/WN) sub-tile made of 16x16 MFMA tiles.  Every K group of A,
-// B, the activation scales and the weight-block scales is copied HBM->LDS by
-// direct buffer_load ... lds (no register staging) into one of STAGES LDS
-// buffers; STAGES-1 groups are in flight while one feeds the MFMAs, and the
-// copies of the next group are spread between the MFMA rows.  LDS rows are
-// 128 bytes; the eight 16-byte chunks of a row are stored XOR-swizzled
-// (lds_swizzle) so that the fragment reads are free of bank conflicts.  The
-// lane K order inside an MFMA operand (32 bytes = chunks 2g, 2g+1 for lane
-// group g) is the same for A and B, so products pair matching K.  Each
-// MFMA's FP32 promotion is issued a few MFMAs later (a ring of partial
-// products), so the VALU multiply-adds overlap the matrix cores.
+// (BM/WM) x (BN/WN) sub-tile made of 16x16 MFMA tiles.  Every K group of A
+// and B is copied HBM->LDS by direct buffer_load ... lds (no register
+// staging) into one of STAGES LDS buffers; the group's scales go through
+// registers into a separate LDS array.  STAGES-1 groups are in flight while
+// one feeds the MFMAs, and the copies of the next group are spread between
+// the MFMA rows.  LDS rows are 128 bytes; the eight 16-byte chunks of a row
+// are stored XOR-swizzled (lds_swizzle) so that the fragment reads are free
+// of bank conflicts.  The lane K order inside an MFMA operand (32 bytes =
+// chunks 2g, 2g+1 for lane group g) is the same for A and B, so products
+// pair matching K.  Each MFMA's FP32 promotion is issued a few MFMAs later
+// (a ring of partial products), so the VALU multiply-adds overlap the matrix
+// cores.  B rows are staged permuted within each wave's columns so that a
+// lane's MFMA columns are consecutive output columns (vector stores).
+//
+// Variants: fp32, bf16 or E4M3 output (the last quantized per 1x128 tile
+// along N in the epilogue, the next GEMM's input); B scaled per 128x128
+// block or, with RowScaledB, per row and K group (weight gradients); dense
+// or grouped (MoE) tile schedules.
 #pragma once
 
 #include "device.hpp"
@@ -109,6 +116,15 @@ struct TileCoords {
   int64_t row0, row_end, col0;
   const uint8_t* b;
   const float* sb;
+  int64_t kb0, KB;  // the tile's K groups: kb0 .. kb0 + KB - 1 (KB >= 1)
+  void* c;          // output matrix of the tile (row0, col0 relative to it)
+};
+
+// Tile schedules of one launch.
+enum Sched {
+  kDense = 0,     // one GEMM
+  kGroupRows = 1, // row ranges of A per group, one B per group (MoE forward)
+  kGroupK = 2     // K ranges per group, one C per group (MoE weight gradient)
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
@@ -142,6 +158,30 @@ __device__ __forceinline__ void dense_tile(const GemmArgs& p, int64_t i, TileCoo
   t.sb = p.sb;
   t.row0 = tm * C::BM;
   t.row_end = p.M;
+  t.kb0 = 0;
+  t.KB = p.K / 128;
+  t.c = p.c;
+}
+
+// Grouped along K: group g owns the K range [off[g], off[g+1]) (multiples of
+// 128) and its own output C_g = c + g * c_group_stride; every group has the
+// same MT x NT tiles, walked group after group.  KB == 0 for an empty group.
+template <class C>
+__device__ __forceinline__ void kgrouped_tile(const GemmArgs& p, int64_t i, TileCoords& t,
+                                              int out_bytes) {
+  const int64_t MT = (p.M + C::BM - 1) / C::BM;
+  const int64_t per = MT * ((p.N + C::BN - 1) / C::BN);
+  const int64_t g = i / per;
+  int64_t tm;
+  raster<C>(p, i % per, MT, tm, t.col0);
+  t.b = p.b;
+  t.sb = p.sb;
+  t.row0 = tm * C::BM;
+  t.row_end = p.M;
+  const int64_t o0 = p.group_offsets[g], o1 = p.group_offsets[g + 1];
+  t.kb0 = o0 / 128;
+  t.KB = (o1 - o0) / 128;
+  t.c = static_cast<char*>(p.c) + g * p.c_group_stride * out_bytes;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -200,6 +240,9 @@ __device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t i, int64
   t.row_end = p.group_offsets[g + 1];
   t.b = p.b + g * p.b_group_stride;
   t.sb = p.sb + g * NB * p.sb_ld;
+  t.kb0 = 0;
+  t.KB = p.K / 128;
+  t.c = p.c;
 }
 
 // Loop-invariant per-lane byte offsets of one stage's direct copies,
@@ -272,8 +315,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 template <class C>
 __device__ __forceinline__ Rsrc make_rsrc_set(const GemmArgs& p, const TileCoords& t) {
   Rsrc r;
-  r.a = make_rsrc(p.a + t.row0 * p.lda);
-  r.b = make_rsrc(t.b + t.col0 * p.ldb);
+  r.a = make_rsrc(p.a + t.row0 * p.lda + t.kb0 * 128);
+  r.b = make_rsrc(t.b + t.col0 * p.ldb + t.kb0 * 128);
   return r;
 }
 
@@ -297,8 +340,9 @@ template <class C>
 __device__ __forceinline__ void load_scales(const GemmArgs& p, const TileCoords& t,
                                             const LoadPlan<C>& lp, int64_t kb,
                                             float (&v)[C::SREG]) {
-  const float* sa = p.sa + kb * p.ldsa + t.row0;
-  const float* sb = C::ROWB ? t.sb + kb * p.sb_ld + t.col0 : t.sb + (t.col0 / 128) * p.sb_ld + kb;
+  const float* sa = p.sa + (t.kb0 + kb) * p.ldsa + t.row0;
+  const float* sb = C::ROWB ? t.sb + (t.kb0 + kb) * p.sb_ld + t.col0
+                            : t.sb + (t.col0 / 128) * p.sb_ld + t.kb0 + kb;
 #pragma unroll
   for (int s = 0; s < C::SREG; ++s) {
     const int item = (int)threadIdx.x + s * C::THREADS;
@@ -521,9 +565,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoords& 
   using T = typename std::conditional<OUT == kOutBF16, uint16_t, float>::type;
   const int g4 = lane >> 4, l16 = lane & 15;
   const int64_t col = t.col0 + wn * C::TN + C::FN * l16;
-  const bool vec = C::FN > 1 && reinterpret_cast<uintptr_t>(p.c) % (C::FN * sizeof(T)) == 0 &&
+  const bool vec = C::FN > 1 && reinterpret_cast<uintptr_t>(t.c) % (C::FN * sizeof(T)) == 0 &&
                    p.ldc % C::FN == 0;
-  T* const out = reinterpret_cast<T*>(p.c);
+  T* const out = reinterpret_cast<T*>(t.c);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
@@ -602,7 +646,7 @@ __device__ __forceinline__ void store_tile_e4m3(const GemmArgs& p, const TileCoo
   const int64_t col = t.col0 + wn * C::TN + C::FN * l16;
   if (col >= p.N) return;  // the wave's whole 128-column tile is past N
   const int nbw = (wn * C::TN) / 128;
-  uint8_t* const out = reinterpret_cast<uint8_t*>(p.c);
+  uint8_t* const out = reinterpret_cast<uint8_t*>(t.c);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const float4 r4 =
@@ -641,7 +685,7 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int64_t KB = p.K / 128;
+  const int64_t KB = t.KB;
 
   LoadPlan<C> lp;
   make_plan<C>(p, t, wave, lane, lp);
@@ -765,22 +809,36 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
   }
 }
 
+// A tile of a group without K range: C_g = 0 there (fp32 or bf16 output).
+template <class C, int OUT>
+__device__ __forceinline__ void store_zero_tile(const GemmArgs& p, const TileCoords& t) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  v4f zero[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) zero[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  store_tile<C, OUT>(p, t, zero, wave / C::WN, wave % C::WN, threadIdx.x & 63);
+}
+
 // One launch covers the raster of BM x BN tiles.
-// Dense: when the raster would end in a partial round of workgroups (fewer
-// tiles than compute units left for the last round), its last tiles are
-// split into two TAIL (half-height) tiles each, so the last round takes half
-// as long: workgroups [0, full) take whole tiles, the rest take half tiles.
-// Grouped: the grid is an upper bound on the tile count (the group sizes live
-// on the device); the workgroups past the real count exit at once, and a
-// group's last tile-row runs as a TAIL tile when it holds at most TAIL::BM
-// rows.  TAIL == C: no half tiles.
+// Dense and grouped-along-K: when the raster would end in a partial round of
+// workgroups (fewer tiles than compute units left for the last round), its
+// last tiles are split into two TAIL (half-height) tiles each, so the last
+// round takes half as long: workgroups [0, full) take whole tiles, the rest
+// take half tiles.
+// Grouped rows: the grid is an upper bound on the tile count (the group
+// sizes live on the device); the workgroups past the real count exit at
+// once, and a group's last tile-row runs as a TAIL tile when it holds at
+// most TAIL::BM rows.  TAIL == C: no half tiles.
 // The buffer-resource type exists only for the device; the host pass sees an
 // empty kernel (it only needs the launch stub).
-template <class C, class TAIL, bool GROUPED, int OUT>
+template <class C, class TAIL, int SCHED, int OUT>
 __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int64_t full) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(TAIL::THREADS == C::THREADS && TAIL::BN == C::BN && 2 * TAIL::BM == C::BM ||
                     std::is_same<C, TAIL>::value, "tail tiles are half-height tiles");
+  static_assert(SCHED != kGroupK || OUT != kOutE4M3, "grouped-K output is fp32 or bf16");
   constexpr int SB = C::STAGE_BYTES > TAIL::STAGE_BYTES ? C::STAGE_BYTES : TAIL::STAGE_BYTES;
   constexpr int SF = C::SCALE_FLOATS > TAIL::SCALE_FLOATS ? C::SCALE_FLOATS : TAIL::SCALE_FLOATS;
   constexpr int NS = C::STAGES > TAIL::STAGES ? C::STAGES : TAIL::STAGES;
@@ -799,7 +857,7 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
   const LdsSet L{{st0, st1, st2, st3}, {sc0, sc1, sc2, sc3}, red, rcp};
   const int64_t bid = blockIdx.x;
   TileCoords t;
-  if constexpr (GROUPED) {
+  if constexpr (SCHED == kGroupRows) {
     (void)full;
     const int64_t MT = grouped_row_tiles<C>(p);
     const int64_t T = MT * ((p.N + C::BN - 1) / C::BN);
@@ -813,14 +871,34 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
     }
     block_gemm_body<C, OUT>(p, t, L);
   } else {
+    constexpr int out_bytes = OUT == kOutF32 ? 4 : OUT == kOutBF16 ? 2 : 1;
+    auto tile_of = [&](int64_t i) {
+      if constexpr (SCHED == kGroupK) {
+        kgrouped_tile<C>(p, i, t, out_bytes);
+      } else {
+        dense_tile<C>(p, i, t);
+      }
+    };
     if (bid < full) {
-      dense_tile<C>(p, xcd_remap(bid, full), t);
+      tile_of(xcd_remap(bid, full));
+      if constexpr (SCHED == kGroupK) {
+        if (t.KB == 0) {  // whole workgroup: a group without K range
+          store_zero_tile<C, OUT>(p, t);
+          return;
+        }
+      }
       block_gemm_body<C, OUT>(p, t, L);
     } else if constexpr (HALVES) {
       const int64_t j = xcd_remap(bid - full, (int64_t)gridDim.x - full);
-      dense_tile<C>(p, full + j / 2, t);
+      tile_of(full + j / 2);
       t.row0 += (j & 1) * TAIL::BM;
       if (t.row0 >= t.row_end) return;  // lower half below the last row
+      if constexpr (SCHED == kGroupK) {
+        if (t.KB == 0) {
+          store_zero_tile<TAIL, OUT>(p, t);
+          return;
+        }
+      }
       block_gemm_body<TAIL, OUT>(p, t, L);
     }
   }
@@ -840,17 +918,18 @@ inline int device_cus() {
   return cached[dev];
 }
 
-template <class C, bool GROUPED, class TAIL = C>
+template <class C, int SCHED, class TAIL = C>
 hipError_t launch(const GemmArgs& args, OutKind out, hipStream_t stream) {
   const int64_t NT = (args.N + C::BN - 1) / C::BN;
-  // grouped: every non-empty group adds at most one partial tile-row, and
-  // every tile-row holds at least one row
   int64_t MT = (args.M + C::BM - 1) / C::BM;
-  if (GROUPED) MT = MT + args.G < args.M ? MT + args.G : args.M;
-  const int64_t tiles = MT * NT;
+  // grouped rows: every non-empty group adds at most one partial tile-row,
+  // and every tile-row holds at least one row
+  if (SCHED == kGroupRows) MT = MT + args.G < args.M ? MT + args.G : args.M;
+  // grouped K: the same tiles for every group
+  const int64_t tiles = MT * NT * (SCHED == kGroupK ? args.G : 1);
   if (tiles <= 0) return hipSuccess;
   int64_t full = tiles, blocks = tiles;
-  if (!GROUPED && !std::is_same<C, TAIL>::value) {
+  if (SCHED != kGroupRows && !std::is_same<C, TAIL>::value) {
     const int64_t cus = device_cus();
     if (cus > 0 && tiles > cus && tiles % cus != 0) {
       full = tiles / cus * cus;
@@ -861,16 +940,16 @@ hipError_t launch(const GemmArgs& args, OutKind out, hipStream_t stream) {
   const dim3 grid((unsigned)blocks), block(C::THREADS);
   switch (out) {
     case kOutF32:
-      hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, kOutF32>), grid, block, 0, stream,
+      hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, SCHED, kOutF32>), grid, block, 0, stream,
                          args, full);
       break;
     case kOutBF16:
-      hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, kOutBF16>), grid, block, 0, stream,
+      hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, SCHED, kOutBF16>), grid, block, 0, stream,
                          args, full);
       break;
     default:
-      if constexpr (C::BN % 128 == 0 && !C::ROWB) {
-        hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, GROUPED, kOutE4M3>), grid, block, 0,
+      if constexpr (C::BN % 128 == 0 && !C::ROWB && SCHED != kGroupK) {
+        hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, SCHED, kOutE4M3>), grid, block, 0,
                            stream, args, full);
       } else {
         // E4M3 output needs whole 128-column tiles; row-scaled B (weight

@@ -26,6 +26,7 @@ struct GemmArgs {
   int64_t K;
   const int32_t* group_offsets;  // grouped only, device, G+1 entries
   int64_t G;
+  int64_t c_group_stride;        // grouped along K: elements between the groups' outputs
 };
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -54,6 +55,11 @@ hipError_t launch_block_gemm(const GemmArgs& args, OutKind out, hipStream_t stre
 
 // B scaled per row and 128-K group: sb(n, kb) at sb[kb*sb_ld + n]
 hipError_t launch_block_gemm_rowscaled(const GemmArgs& args, OutKind out, hipStream_t stream);
+
+// Row-scaled B, grouped along K: group g contracts over K range
+// [off[g], off[g+1]) (multiples of 128) into C + g*c_group_stride.
+hipError_t launch_kgrouped_gemm_rowscaled(const GemmArgs& args, OutKind out,
+                                          hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, OutKind out, hipStream_t stream);
 

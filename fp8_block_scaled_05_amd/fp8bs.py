@@ -31,6 +31,7 @@ EXPORTS = (
     "fp8_block_gemm_e4m3_out",
     "fp8_block_grouped_gemm_e4m3_out",
     "fp8_block_gemm_rowscaled",
+    "fp8_block_kgrouped_gemm_rowscaled",
     "fp8bs_workspace_bytes",
     "fp8bs_status_string",
     "fp8bs_last_hip_error",
@@ -50,6 +51,8 @@ _SIGNATURES = {
     "fp8_quant_act_128x1_t": ([_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _int),
     "fp8_block_gemm_rowscaled": ([_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _int, _i64,
                                   _i64, _i64, _p], _int),
+    "fp8_block_kgrouped_gemm_rowscaled": ([_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64,
+                                           _int, _p, _i64, _i64, _i64, _i64, _p], _int),
     "fp8_block_gemm": ([_int, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _int,
                         _i64, _i64, _i64, _p, _sz, _p], _int),
     "fp8_block_grouped_gemm": ([_p, _i64, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _int,
@@ -243,6 +246,29 @@ def fp8_block_gemm_rowscaled(a, sa, b, sb, out=None, out_dtype=torch.float32):
                                         _ptr(sb), sb.shape[1], _ptr(out), _ld(out),
                                         _out_kind(out.dtype), M, N, K, _stream(a)),
            "fp8_block_gemm_rowscaled")
+    return out
+
+
+def fp8_block_kgrouped_gemm_rowscaled(a, sa, b, sb, group_offsets, out=None,
+                                      out_dtype=torch.float32):
+    """MoE weight gradients in one launch: out[g] = A[:, t0:t1] . B[:, t0:t1]^T
+    over expert g's token columns [t0, t1) = group_offsets[g:g+2]
+    (multiples of 128).  ``a`` [M][T], ``b`` [N][T] from
+    ``fp8_quant_act_128x1_t``; returns ``out`` [G][M][N]."""
+    _need_device(a, sa, b, sb, group_offsets, out)
+    if group_offsets.dtype != torch.int32:
+        raise ValueError("group_offsets must be int32")
+    M, T = a.shape
+    N = b.shape[0]
+    G = group_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty(G, M, N, dtype=out_dtype, device=a.device)
+    if out.dim() != 3 or out.stride(2) != 1:
+        raise ValueError("out must be [G][M][N] with unit column stride")
+    _check(lib.fp8_block_kgrouped_gemm_rowscaled(
+        _ptr(a), _ld(a), _ptr(sa), sa.shape[1], _ptr(b), _ld(b), _ptr(sb), sb.shape[1], _ptr(out),
+        out.stride(1), out.stride(0), _out_kind(out.dtype), _ptr(group_offsets), G, M, N, T,
+        _stream(a)), "fp8_block_kgrouped_gemm_rowscaled")
     return out
 
 

@@ -279,6 +279,40 @@ int fp8_block_gemm_rowscaled(const uint8_t* a, int64_t lda, const float* sa,
                              int64_t ldc, int out_kind, int64_t M, int64_t N,
                              int64_t K, void* stream);
 /*
+ * MoE weight gradients in one launch: for every expert g,
+ *   C_g[M][N] = A[:, t0:t1] . B[:, t0:t1]^T,  [t0, t1) = [off[g], off[g+1]),
+ * the row-scaled GEMM of fp8_block_gemm_rowscaled over the expert's token
+ * columns.  A = dY^T and B = X^T of all experts' tokens, each expert's tokens
+ * zero-padded to a multiple of 128 (zero rows raise no maximum and add
+ * nothing), both quantized by fp8_quant_act_128x1_t.
+ * Pages: "Advantages of using FP8 for GEMM operations in DeepSeek-V3",
+ * items 5 and 8 (FP8 GEMMs with FP32 promotion, for dense and MoE layers);
+ * "How the unified E4M3 format adds to DeepSeek-V3's efficiency", section
+ * "Fine-grained quantization strategy" (the same format in the backward
+ * pass).
+ *
+ *   a, sa   codes [M][lda] (lda >= K_total), sa(m, j) at sa[j*ldsa + m] for
+ *           the 128-token groups j = 0 .. K_total/128 - 1.
+ *   b, sb   codes [N][ldb], sb(n, j) at sb[j*ldsb + n].
+ *   c       outputs: C_g starts at c + g*c_group_stride (elements), rows of
+ *           ldc; fp32 or bf16 by out_kind.  An expert without tokens gets
+ *           C_g = 0.
+ *   group_offsets DEVICE int32 [G+1], 0 = off[0] <= ... <= off[G] = K_total,
+ *           every offset a multiple of 128.  Trusted, not validated.
+ * Errors: as fp8_block_gemm_rowscaled; G outside [1, 4096] or K_total not a
+ *         multiple of 128 -> ERR_SHAPE; c_group_stride < (M-1)*ldc + N ->
+ *         ERR_LAYOUT.
+ */
+int fp8_block_kgrouped_gemm_rowscaled(const uint8_t* a, int64_t lda,
+                                      const float* sa, int64_t ldsa,
+                                      const uint8_t* b, int64_t ldb,
+                                      const float* sb, int64_t ldsb, void* c,
+                                      int64_t ldc, int64_t c_group_stride,
+                                      int out_kind,
+                                      const int32_t* group_offsets, int64_t G,
+                                      int64_t M, int64_t N, int64_t K_total,
+                                      void* stream);
+/*
  * Grouped (MoE) block-scaled FP8 GEMM: rows group_offsets[g] ..
  * group_offsets[g+1]-1 of A are multiplied by expert g's weight.
  * Pages: "Advantages of using FP8 for GEMM operations in DeepSeek-V3",

@@ -235,6 +235,24 @@ def test_backward_calls_validation(fp8bs):
     assert rs(b=P + 8) == fp8bs.ERR_LAYOUT
 
 
+def test_kgrouped_validation(fp8bs):
+    lib = fp8bs.lib
+
+    def k(a=P, lda=256, sa=P, ldsa=64, b=P, ldb=256, sb=P, ldsb=128, c=P, ldc=128,
+          cstride=64 * 128, out_kind=0, off=P, G=2, M=64, N=128, T=256):
+        return lib.fp8_block_kgrouped_gemm_rowscaled(a, lda, sa, ldsa, b, ldb, sb, ldsb, c, ldc,
+                                                     cstride, out_kind, off, G, M, N, T, None)
+
+    assert k(out_kind=2) == fp8bs.ERR_DTYPE
+    assert k(G=0) == fp8bs.ERR_SHAPE
+    assert k(T=200) == fp8bs.ERR_SHAPE
+    assert k(M=0) == fp8bs.OK
+    assert k(off=0) == fp8bs.ERR_NULL
+    assert k(cstride=64 * 128 - 1) == fp8bs.ERR_LAYOUT
+    assert k(lda=128) == fp8bs.ERR_LAYOUT
+    assert k(ldsb=100) == fp8bs.ERR_LAYOUT
+
+
 def test_workspace_query(fp8bs):
     lib = fp8bs.lib
     assert lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_E4M3, 64, 128, 256, 0) == 0

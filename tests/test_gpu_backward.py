@@ -267,3 +267,52 @@ def test_moe_weight_gradient_per_expert(fp8bs):
         gu.assert_same_bits(gu.host(qa), qa_o, f"expert {g} dY^T codes")
         gu.assert_same_bits(gu.host(qb), qb_o, f"expert {g} X^T codes")
         gu.check_gemm(dw, C, B)
+
+
+def _token_groups(sizes, M, N, case):
+    """Per-expert dY [mg][M] and X [mg][N], zero-padded to multiples of 128 and
+    concatenated; returns the padded bf16 tensors and the padded offsets."""
+    padded = [(mg + 127) // 128 * 128 for mg in sizes]
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    T = int(offsets[-1])
+    dy = torch.zeros(T, M, dtype=torch.bfloat16)
+    x = torch.zeros(T, N, dtype=torch.bfloat16)
+    for g, mg in enumerate(sizes):
+        if mg:
+            dy[offsets[g]:offsets[g] + mg] = synth.act(mg, M, case=case, tensor=g)
+            x[offsets[g]:offsets[g] + mg] = synth.act(mg, N, case=case, tensor=100 + g)
+    return dy, x, offsets
+
+
+@pytest.mark.parametrize("sizes,M,N,out,gpu_quant", [
+    ([200, 0, 70, 300], 300, 200, torch.float32, False),  # ragged rows/cols, an empty expert
+    ([128] * 20, 1024, 1024, torch.float32, True),        # 320 tiles: last round as half tiles
+    ([129, 1, 256], 256, 384, torch.bfloat16, True),
+])
+def test_kgrouped_weight_gradient(fp8bs, sizes, M, N, out, gpu_quant):
+    """One launch over all experts against the oracle, expert by expert; the
+    operands come from the GPU quantizers (checked bit for bit) or, for
+    feature sizes the transposed quantizer does not take, from the oracle."""
+    dy, x, offsets = _token_groups(sizes, M, N, case=880 + len(sizes))
+    qa_o, sa_o = oracle.quant_act_128x1_t(synth.bf16_bits(dy))
+    qb_o, sb_o = oracle.quant_act_128x1_t(synth.bf16_bits(x))
+    if gpu_quant:
+        qa, sa = fp8bs.fp8_quant_act_128x1_t(dy.cuda())
+        qb, sb = fp8bs.fp8_quant_act_128x1_t(x.cuda())
+        torch.cuda.synchronize()
+        gu.assert_same_bits(gu.host(qa), qa_o, "dY^T codes")
+        gu.assert_same_bits(gu.host(qb), qb_o, "X^T codes")
+    else:
+        qa, sa, qb, sb = gu.u8(qa_o), gu.f32(sa_o), gu.u8(qb_o), gu.f32(sb_o)
+    G = len(sizes)
+    dw = torch.full((G, M, N), 5.0, dtype=out, device="cuda")
+    fp8bs.fp8_block_kgrouped_gemm_rowscaled(qa, sa, qb, sb, torch.from_numpy(offsets).cuda(),
+                                            out=dw)
+    torch.cuda.synchronize()
+    C, B = oracle.kgrouped_gemm_rowscaled(qa_o, sa_o, qb_o, sb_o, offsets)
+    dwh = gu.host_f64(dw)
+    for g in range(G):
+        if sizes[g] == 0:
+            assert np.all(dwh[g] == 0.0), f"expert {g} without tokens must be zero"
+        else:
+            gu.check_gemm(dwh[g], C[g], B[g], bf16=out == torch.bfloat16)
