@@ -13,8 +13,9 @@ path: the activation and weight quantizers alone at 8192x7168 / 18432x7168
 (32 experts, top-8 of 4096 tokens, gate/up and down), the skinny GEMM with
 in-call activation quantization (M = 16, 64), the dense GEMM with its output
 quantized for the next FP8 GEMM (against bf16 output followed by the
-activation quantizer), the backward pass of the dense layer (data and weight
-gradients with their quantizers), online against delayed (history-based) scaling on a
+activation quantizer), the backward pass of the dense layer and of the MoE
+gate/up layer (data and weight gradients with their quantizers), online
+against delayed (history-based) scaling on a
 drifting sequence of activations (quantization error, clipped and flushed
 fractions), and the CPU oracle on a bounded sample of the dense step
 (``cpu_baseline``).
@@ -119,6 +120,8 @@ def _dense_setup(torch, fp8bs, synth):
 
 
 def _parts(torch, fp8bs, synth, dense, iters=30):
+    import numpy as np
+
     out = {}
     tm = Timer(torch)
 
@@ -246,6 +249,61 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         "gemms_TFLOPs": (f1 + f2) / (g1 + g2) / 1e9,
         "gemms_frac_mfma": (f1 + f2) / (g1 + g2) / 1e9 / PEAK_FP8_TFLOPS,
         "step_with_quant_us": tot * 1e3, "step_TFLOPs": (f1 + f2) / tot / 1e9}
+    del a2, w2, qa2, sa2, qw2, sw2, c2, c1
+
+    # MoE backward of the gate/up layer (same routing): data gradient
+    # dX = dY . W_g (grouped GEMM over per-expert transposed weights) and
+    # weight gradients dW_g = dY_g^T . X_g (one launch over the experts'
+    # 128-padded token ranges)
+    dy1 = synth.act(Mt, 4096, case=synth.MOE.case_id, tensor=2, device="cuda")
+    qwt = torch.empty(G, 7168, 4096, dtype=torch.uint8, device="cuda")
+    swt = torch.empty(G, 56, 32, dtype=torch.float32, device="cuda")
+    for g in range(G):
+        fp8bs.fp8_quant_w_128x128_t(w1[g], qw1[g], sw1[g], qwt[g], swt[g])
+    del w1, qw1, sw1
+    sizes = offsets[1:] - offsets[:-1]
+    poff = np.concatenate([[0], np.cumsum((sizes + 127) // 128 * 128)]).astype(np.int32)
+    Tp = int(poff[-1])
+    dyp = torch.zeros(Tp, 4096, dtype=torch.bfloat16, device="cuda")
+    xp = torch.zeros(Tp, 7168, dtype=torch.bfloat16, device="cuda")
+    for g in range(G):
+        n = int(sizes[g])
+        dyp[poff[g]:poff[g] + n] = dy1[offsets[g]:offsets[g] + n]
+        xp[poff[g]:poff[g] + n] = a1[offsets[g]:offsets[g] + n]
+    poff_d = torch.from_numpy(poff).cuda()
+    qdy1 = torch.empty(Mt, 4096, dtype=torch.uint8, device="cuda")
+    sdy1 = torch.empty(32, Mt, dtype=torch.float32, device="cuda")
+    dx1 = torch.empty(Mt, 7168, dtype=torch.bfloat16, device="cuda")
+    qdyt = torch.empty(4096, Tp, dtype=torch.uint8, device="cuda")
+    sdyt = torch.empty(Tp // 128, 4096, dtype=torch.float32, device="cuda")
+    qxt = torch.empty(7168, Tp, dtype=torch.uint8, device="cuda")
+    sxt = torch.empty(Tp // 128, 7168, dtype=torch.float32, device="cuda")
+    dw1 = torch.empty(G, 4096, 7168, dtype=torch.float32, device="cuda")
+
+    def moe_bwd(timed):
+        run = tm.run if timed else (lambda n, f: f())
+        run("mb_q", lambda: (fp8bs.fp8_quant_act_1x128(dy1, qdy1, sdy1),
+                             fp8bs.fp8_quant_act_128x1_t(dyp, qdyt, sdyt),
+                             fp8bs.fp8_quant_act_128x1_t(xp, qxt, sxt)))
+        run("mb_dx", lambda: fp8bs.fp8_block_grouped_gemm(qdy1, sdy1, qwt, swt, off_d, out=dx1))
+        run("mb_dw", lambda: fp8bs.fp8_block_kgrouped_gemm_rowscaled(qdyt, sdyt, qxt, sxt, poff_d,
+                                                                     out=dw1))
+
+    for i in range(3):
+        moe_bwd(False)
+    for i in range(10):
+        moe_bwd(True)
+    fdx = 2.0 * Mt * 4096 * 7168
+    fdw = 2.0 * Tp * 4096 * 7168  # padded tokens included (zero rows)
+    tdx, tdw, tq = tm.avg_ms("mb_dx"), tm.avg_ms("mb_dw"), tm.avg_ms("mb_q")
+    out["moe_backward_gate_up_E32_top8_T4096"] = {
+        "tokens_padded": Tp,
+        "dgrad_us": tdx * 1e3, "dgrad_TFLOPs": fdx / tdx / 1e9,
+        "wgrad_us": tdw * 1e3, "wgrad_TFLOPs": fdw / tdw / 1e9,
+        "wgrad_useful_TFLOPs": fdx / tdw / 1e9,
+        "quantizers_us": tq * 1e3}
+    del dy1, qwt, swt, dyp, xp, qdy1, sdy1, dx1, qdyt, sdyt, qxt, sxt, dw1, a1
+    torch.cuda.empty_cache()
 
     # backward pass of the dense layer (tokens 4096, N=18432, K=7168):
     # quantizers with transposed outputs, data gradient dX = dY . W
