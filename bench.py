@@ -146,6 +146,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         "frac_mfma": 2.0 * M * N * K / ms / 1e9 / PEAK_FP8_TFLOPS,
         "unfused_bf16_gemm_then_act_quant_us": ms2 * 1e3}
     del qc, scq, cb, qc2, sc2
+    torch.cuda.empty_cache()
 
     # activation quantizer 8192x7168, 4 rotated buffer sets (712 MB)
     Mq, Kq = 8192, 7168
@@ -162,6 +163,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
                                   "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
                                   "bytes": byt}
     del xs, qs, ss
+    torch.cuda.empty_cache()
 
     # weight quantizer 18432x7168, 2 rotated sets (793 MB)
     ws = [synth.weight(N, K, case=synth.QUANT.case_id, tensor=10 + i, device="cuda") for i in range(2)]
@@ -196,6 +198,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
             "us": ms * 1e3, "GBps": byt / ms / 1e6, "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
             "TFLOPs": 2 * Ms * N * K / ms / 1e9, "bytes": byt}
     del wq
+    torch.cuda.empty_cache()
 
     # grouped MoE: 4096 tokens, top-8 of 32 experts; gate/up N=4096 K=7168,
     # down N=7168 K=2048; step = quantize A's and all expert weights + 2 GEMMs
@@ -351,6 +354,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         "wgrad_frac_mfma": fl / t["b_dw"] / 1e9 / PEAK_FP8_TFLOPS,
         "step_us": sum(t.values()) * 1e3}
     del dy, xb, wb, bq, bs, bqt, bst, qdy, sdy, qdyt, sdyt, qxt, sxt, dx, dw
+    torch.cuda.empty_cache()
 
     # online vs delayed scaling on drifting activations (quality, not speed)
     from fp8_block_scaled_05_amd import ablation
