@@ -107,6 +107,14 @@ class Timer:
         ps = self.pairs.get(name, [])
         return sum(a.elapsed_time(b) for a, b in ps) / len(ps) if ps else float("nan")
 
+    def med_ms(self, name):
+        """Median over the calls: the per-workload figures of ``parts`` (a
+        single stalled call, seen now and then on the boxes, would otherwise
+        move a mean over 10-30 calls)."""
+        self.torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in self.pairs.get(name, []))
+        return ts[len(ts) // 2] if ts else float("nan")
+
 
 def _dense_setup(torch, fp8bs, synth):
     a = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
@@ -140,7 +148,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         f2 = lambda: (fp8bs.fp8_block_gemm(qa, sa, qw, sw, out=cb),
                       fp8bs.fp8_quant_act_1x128(cb, qc2, sc2))
         (tm.run("gemm_then_q", f2) if i >= 5 else f2())
-    ms, ms2 = tm.avg_ms("gemm_q"), tm.avg_ms("gemm_then_q")
+    ms, ms2 = tm.med_ms("gemm_q"), tm.med_ms("gemm_then_q")
     out["dense_gemm_e4m3_out_M4096_N18432_K7168"] = {
         "us": ms * 1e3, "TFLOPs": 2.0 * M * N * K / ms / 1e9,
         "frac_mfma": 2.0 * M * N * K / ms / 1e9 / PEAK_FP8_TFLOPS,
@@ -157,7 +165,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         j = i % 4
         f = lambda: fp8bs.fp8_quant_act_1x128(xs[j], qs[j], ss[j])
         (tm.run("qa", f) if i >= 5 else f())
-    ms = tm.avg_ms("qa")
+    ms = tm.med_ms("qa")
     byt = Mq * Kq * 3.03125
     out["act_quant_8192x7168"] = {"us": ms * 1e3, "GBps": byt / ms / 1e6,
                                   "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
@@ -173,7 +181,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         j = i % 2
         f = lambda: fp8bs.fp8_quant_w_128x128(ws[j], qws[j], sws[j])
         (tm.run("qw", f) if i >= 5 else f())
-    ms = tm.avg_ms("qw")
+    ms = tm.med_ms("qw")
     byt = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
     out["weight_quant_18432x7168"] = {"us": ms * 1e3, "GBps": byt / ms / 1e6,
                                       "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS, "bytes": byt}
@@ -192,7 +200,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
             q, s = wq[i % 4]
             f = lambda: fp8bs.fp8_block_gemm(x, sa_o, q, s, out=cs, workspace=wsp)
             (tm.run(name, f) if i >= 5 else f())
-        ms = tm.avg_ms(name)
+        ms = tm.med_ms(name)
         byt = N * K + (N // 128) * (K // 128) * 4 + Ms * K * 2 + Ms * N * 2
         out[f"skinny_fused_M{Ms}_N18432_K7168"] = {
             "us": ms * 1e3, "GBps": byt / ms / 1e6, "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
@@ -243,8 +251,8 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         moe_step(True)
     f1 = 2.0 * Mt * 4096 * 7168
     f2 = 2.0 * Mt * 7168 * 2048
-    g1, g2 = tm.avg_ms("moe_g1"), tm.avg_ms("moe_g2")
-    tot = g1 + g2 + tm.avg_ms("moe_qa") + tm.avg_ms("moe_qw")
+    g1, g2 = tm.med_ms("moe_g1"), tm.med_ms("moe_g2")
+    tot = g1 + g2 + tm.med_ms("moe_qa") + tm.med_ms("moe_qw")
     out["moe_grouped_E32_top8_T4096"] = {
         "M_total": Mt, "experts_empty": int((offsets[1:] == offsets[:-1]).sum()),
         "gate_up_us": g1 * 1e3, "gate_up_TFLOPs": f1 / g1 / 1e9,
@@ -298,7 +306,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         moe_bwd(True)
     fdx = 2.0 * Mt * 4096 * 7168
     fdw = 2.0 * Tp * 4096 * 7168  # padded tokens included (zero rows)
-    tdx, tdw, tq = tm.avg_ms("mb_dx"), tm.avg_ms("mb_dw"), tm.avg_ms("mb_q")
+    tdx, tdw, tq = tm.med_ms("mb_dx"), tm.med_ms("mb_dw"), tm.med_ms("mb_q")
     out["moe_backward_gate_up_E32_top8_T4096"] = {
         "tokens_padded": Tp,
         "dgrad_us": tdx * 1e3, "dgrad_TFLOPs": fdx / tdx / 1e9,
@@ -340,7 +348,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
     for i in range(iters + 5):
         bwd(i >= 5)
     fl = 2.0 * Mb * N * K
-    t = {k: tm.avg_ms(k) for k in ("b_qw", "b_qdy", "b_qdyt", "b_qxt", "b_dx", "b_dw")}
+    t = {k: tm.med_ms(k) for k in ("b_qw", "b_qdy", "b_qdyt", "b_qxt", "b_dx", "b_dw")}
     out["backward_dense_M4096_N18432_K7168"] = {
         "weight_quant_with_transpose_us": t["b_qw"] * 1e3,
         "weight_quant_with_transpose_GBps": N * K * 4 / t["b_qw"] / 1e6,
