@@ -290,6 +290,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
     qxt = torch.empty(7168, Tp, dtype=torch.uint8, device="cuda")
     sxt = torch.empty(Tp // 128, 7168, dtype=torch.float32, device="cuda")
     dw1 = torch.empty(G, 4096, 7168, dtype=torch.float32, device="cuda")
+    dw1b = torch.empty(G, 4096, 7168, dtype=torch.bfloat16, device="cuda")
 
     def moe_bwd(timed):
         run = tm.run if timed else (lambda n, f: f())
@@ -299,6 +300,8 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         run("mb_dx", lambda: fp8bs.fp8_block_grouped_gemm(qdy1, sdy1, qwt, swt, off_d, out=dx1))
         run("mb_dw", lambda: fp8bs.fp8_block_kgrouped_gemm_rowscaled(qdyt, sdyt, qxt, sxt, poff_d,
                                                                      out=dw1))
+        run("mb_dw16", lambda: fp8bs.fp8_block_kgrouped_gemm_rowscaled(qdyt, sdyt, qxt, sxt,
+                                                                       poff_d, out=dw1b))
 
     for i in range(3):
         moe_bwd(False)
@@ -312,8 +315,10 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         "dgrad_us": tdx * 1e3, "dgrad_TFLOPs": fdx / tdx / 1e9,
         "wgrad_us": tdw * 1e3, "wgrad_TFLOPs": fdw / tdw / 1e9,
         "wgrad_useful_TFLOPs": fdx / tdw / 1e9,
+        "wgrad_bf16_out_us": tm.med_ms("mb_dw16") * 1e3,
+        "wgrad_bf16_out_TFLOPs": fdw / tm.med_ms("mb_dw16") / 1e9,
         "quantizers_us": tq * 1e3}
-    del dy1, qwt, swt, dyp, xp, qdy1, sdy1, dx1, qdyt, sdyt, qxt, sxt, dw1, a1
+    del dy1, qwt, swt, dyp, xp, qdy1, sdy1, dx1, qdyt, sdyt, qxt, sxt, dw1, dw1b, a1
     torch.cuda.empty_cache()
 
     # backward pass of the dense layer (tokens 4096, N=18432, K=7168):

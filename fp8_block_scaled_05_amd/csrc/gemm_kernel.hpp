@@ -879,8 +879,14 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
         dense_tile<C>(p, i, t);
       }
     };
+    // grouped along K: the groups' K lengths differ, so contiguous runs per
+    // XCD (equal tile counts) would give the XCDs unequal work; dealing
+    // the tiles round-robin gives every XCD tiles of every group
+    auto order = [&](int64_t i, int64_t n) {
+      return SCHED == kGroupK ? i : xcd_remap(i, n);
+    };
     if (bid < full) {
-      tile_of(xcd_remap(bid, full));
+      tile_of(order(bid, full));
       if constexpr (SCHED == kGroupK) {
         if (t.KB == 0) {  // whole workgroup: a group without K range
           store_zero_tile<C, OUT>(p, t);
@@ -889,7 +895,7 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
       }
       block_gemm_body<C, OUT>(p, t, L);
     } else if constexpr (HALVES) {
-      const int64_t j = xcd_remap(bid - full, (int64_t)gridDim.x - full);
+      const int64_t j = order(bid - full, (int64_t)gridDim.x - full);
       tile_of(full + j / 2);
       t.row0 += (j & 1) * TAIL::BM;
       if (t.row0 >= t.row_end) return;  // lower half below the last row
