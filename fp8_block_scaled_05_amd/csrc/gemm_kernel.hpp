@@ -131,6 +131,8 @@ enum Sched {
 // b mod 8): give each XCD a contiguous run of the raster of T tiles (the
 // first T mod 8 XCDs one tile more than the others), so that concurrently
 // resident tiles of one XCD share A and B in its L2.  A bijection of [0, T).
+// Used where all tiles cost the same (dense); the grouped schedules, whose
+// tiles differ in cost, keep the round-robin order instead.
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t T) {
   const int64_t x = bid % 8, q = T / 8, r = T % 8;
   return x * q + (x < r ? x : r) + bid / 8;
@@ -862,7 +864,9 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
     const int64_t MT = grouped_row_tiles<C>(p);
     const int64_t T = MT * ((p.N + C::BN - 1) / C::BN);
     if (bid >= T) return;  // whole workgroup: past the last real tile
-    grouped_tile<C>(p, xcd_remap(bid, T), MT, t);
+    // tiles dealt round-robin over the XCDs (not in contiguous runs): the
+    // groups' short last tile-rows and the raster's end then spread evenly
+    grouped_tile<C>(p, bid, MT, t);
     if constexpr (HALVES) {
       if (t.row_end - t.row0 <= TAIL::BM) {
         block_gemm_body<TAIL, OUT>(p, t, L);
