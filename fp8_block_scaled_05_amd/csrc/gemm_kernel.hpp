@@ -825,10 +825,9 @@ __device__ __forceinline__ void store_zero_tile(const GemmArgs& p, const TileCoo
 
 // One launch covers the raster of BM x BN tiles.
 // Dense and grouped-along-K: when the raster would end in a partial round of
-// workgroups (fewer tiles than compute units left for the last round), its
-// last tiles are split into two TAIL (half-height) tiles each, so the last
-// round takes half as long: workgroups [0, full) take whole tiles, the rest
-// take half tiles.
+// at most half the compute units' worth of tiles, those last tiles are split
+// into two TAIL (half-height) tiles each, so the last round takes half as
+// long: workgroups [0, full) take whole tiles, the rest take half tiles.
 // Grouped rows: the grid is an upper bound on the tile count (the group
 // sizes live on the device); the workgroups past the real count exit at
 // once, and a group's last tile-row runs as a TAIL tile when it holds at
@@ -940,10 +939,14 @@ hipError_t launch(const GemmArgs& args, OutKind out, hipStream_t stream) {
   if (tiles <= 0) return hipSuccess;
   int64_t full = tiles, blocks = tiles;
   if (SCHED != kGroupRows && !std::is_same<C, TAIL>::value) {
+    // split the last partial round only when its halves fit in one round
+    // (at most half the compute units' worth of tiles): a larger tail would
+    // take 1.5 rounds of half tiles, longer than one round of whole tiles
     const int64_t cus = device_cus();
-    if (cus > 0 && tiles > cus && tiles % cus != 0) {
-      full = tiles / cus * cus;
-      blocks = full + 2 * (tiles - full);
+    const int64_t tail = cus > 0 ? tiles % cus : 0;
+    if (cus > 0 && tiles > cus && tail != 0 && 2 * tail <= cus) {
+      full = tiles - tail;
+      blocks = full + 2 * tail;
     }
   }
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
