@@ -17,6 +17,11 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool ld_ok(int64_t ld, int64_t row) { return ld >= row && ld % 16 == 0; }
 
+// GEMM operands: the tile copies address up to 256 rows from the tile's
+// first row with 32-bit byte offsets (row * ld + k)
+constexpr int64_t kMaxOperandLd = int64_t(1) << 24;
+bool operand_ld_ok(int64_t ld, int64_t row) { return ld_ok(ld, row) && ld <= kMaxOperandLd; }
+
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int hip_status(hipError_t e) {
@@ -116,7 +121,7 @@ int block_gemm_impl(int a_kind, const void* a, int64_t lda, float* sa, int64_t l
   if (!a || !b || !sb || !c) return FP8BS_ERR_NULL;
   if (a_kind == FP8BS_A_E4M3 && !sa) return FP8BS_ERR_NULL;
   if (out == fp8bs::kOutE4M3 && !sc) return FP8BS_ERR_NULL;
-  if (!ld_ok(lda, K) || !ld_ok(ldb, K) || ldc < N) return FP8BS_ERR_LAYOUT;
+  if (!operand_ld_ok(lda, K) || !operand_ld_ok(ldb, K) || ldc < N) return FP8BS_ERR_LAYOUT;
   if (sa && ldsa < M) return FP8BS_ERR_LAYOUT;
   const uintptr_t c_align = out == fp8bs::kOutF32 ? 4 : out == fp8bs::kOutBF16 ? 2 : 16;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sb, 4) ||
@@ -173,7 +178,8 @@ int grouped_gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ld
   if (M_total == 0 || N == 0) return FP8BS_OK;
   if (!a || !sa || !b || !sb || !c || !group_offsets) return FP8BS_ERR_NULL;
   if (out == fp8bs::kOutE4M3 && !sc) return FP8BS_ERR_NULL;
-  if (!ld_ok(lda, K) || !ld_ok(ldb, K) || ldc < N || ldsa < M_total) return FP8BS_ERR_LAYOUT;
+  if (!operand_ld_ok(lda, K) || !operand_ld_ok(ldb, K) || ldc < N || ldsa < M_total)
+    return FP8BS_ERR_LAYOUT;
   if (b_group_stride % 16 != 0 || b_group_stride < (N - 1) * ldb + K) return FP8BS_ERR_LAYOUT;
   const uintptr_t c_align = out == fp8bs::kOutF32 ? 4 : out == fp8bs::kOutBF16 ? 2 : 16;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sa, 4) ||
@@ -236,7 +242,7 @@ int fp8_block_gemm_rowscaled(const uint8_t* a, int64_t lda, const float* sa, int
   if (M < 0 || N < 0 || K <= 0 || K % kTile != 0) return FP8BS_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BS_OK;
   if (!a || !sa || !b || !sb || !c) return FP8BS_ERR_NULL;
-  if (!ld_ok(lda, K) || !ld_ok(ldb, K) || ldc < N || ldsa < M || ldsb < N)
+  if (!operand_ld_ok(lda, K) || !operand_ld_ok(ldb, K) || ldc < N || ldsa < M || ldsb < N)
     return FP8BS_ERR_LAYOUT;
   const uintptr_t c_align = out_kind == FP8BS_OUT_F32 ? 4 : 2;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sa, 4) ||
@@ -271,8 +277,8 @@ int fp8_block_kgrouped_gemm_rowscaled(const uint8_t* a, int64_t lda, const float
     return FP8BS_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BS_OK;
   if (!a || !sa || !b || !sb || !c || !group_offsets) return FP8BS_ERR_NULL;
-  if (!ld_ok(lda, K_total) || !ld_ok(ldb, K_total) || ldc < N || ldsa < M || ldsb < N ||
-      c_group_stride < (M - 1) * ldc + N)
+  if (!operand_ld_ok(lda, K_total) || !operand_ld_ok(ldb, K_total) || ldc < N || ldsa < M ||
+      ldsb < N || c_group_stride < (M - 1) * ldc + N)
     return FP8BS_ERR_LAYOUT;
   const uintptr_t c_align = out_kind == FP8BS_OUT_F32 ? 4 : 2;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, c_align) || !aligned(sa, 4) ||

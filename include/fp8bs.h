@@ -36,7 +36,9 @@
  *     (partial tiles at the edges are handled); a call with M == 0 or N == 0
  *     returns FP8BS_OK and launches nothing.
  *   - Leading dimensions must be >= the row length and multiples of 16;
- *     tensor pointers must be 16-byte aligned.  Otherwise FP8BS_ERR_LAYOUT.
+ *     tensor pointers must be 16-byte aligned.  The GEMMs' lda and ldb must
+ *     also be at most 2^24 elements, because the tile copies use 32-bit byte
+ *     offsets.  Otherwise FP8BS_ERR_LAYOUT.
  *   - Outputs must not alias inputs.  Calls are thread-safe.
  */
 #ifndef FP8BS_H

@@ -111,6 +111,9 @@ def test_gemm_validation(fp8bs):
     assert _gemm(lib, ldsa=10) == fp8bs.ERR_LAYOUT
     assert _gemm(lib, c=P + 1) == fp8bs.ERR_LAYOUT
     assert _gemm(lib, b=P + 8) == fp8bs.ERR_LAYOUT
+    # the tile copies use 32-bit byte offsets: row strides up to 2^24
+    assert _gemm(lib, lda=2**24 + 16) == fp8bs.ERR_LAYOUT
+    assert _gemm(lib, ldb=2**24 + 16) == fp8bs.ERR_LAYOUT
     # bf16 A needs a workspace of the advertised size
     need = lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_BF16, 64, 128, 256, 0)
     assert need >= 64 * 256 + 2 * 64 * 4
@@ -135,6 +138,7 @@ def test_grouped_validation(fp8bs):
     assert g(bstride=256 * 127) == fp8bs.ERR_LAYOUT
     assert g(bstride=256 * 128 + 8) == fp8bs.ERR_LAYOUT
     assert g(ldsa=32) == fp8bs.ERR_LAYOUT
+    assert g(ldb=2**24 + 16, bstride=(2**24 + 16) * 128) == fp8bs.ERR_LAYOUT
     assert g(out_kind=3) == fp8bs.ERR_DTYPE
 
 
@@ -233,6 +237,7 @@ def test_backward_calls_validation(fp8bs):
     assert rs(ldsb=127) == fp8bs.ERR_LAYOUT
     assert rs(ldsa=63) == fp8bs.ERR_LAYOUT
     assert rs(b=P + 8) == fp8bs.ERR_LAYOUT
+    assert rs(lda=2**24 + 16) == fp8bs.ERR_LAYOUT
 
 
 def test_kgrouped_validation(fp8bs):
@@ -251,6 +256,7 @@ def test_kgrouped_validation(fp8bs):
     assert k(cstride=64 * 128 - 1) == fp8bs.ERR_LAYOUT
     assert k(lda=128) == fp8bs.ERR_LAYOUT
     assert k(ldsb=100) == fp8bs.ERR_LAYOUT
+    assert k(ldb=2**24 + 16) == fp8bs.ERR_LAYOUT
 
 
 def test_workspace_query(fp8bs):
