@@ -79,6 +79,23 @@ int fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, ui
                                           static_cast<hipStream_t>(stream)));
 }
 
+int fp8_quant_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                     int64_t ldq, float* s, int64_t lds, const uint16_t* w, int64_t N,
+                     int64_t ldw, uint8_t* qw, int64_t ldqw, float* sw, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 && N == 0) return FP8BS_OK;
+  if (M > 0 && (!x || !q || !s)) return FP8BS_ERR_NULL;
+  if (N > 0 && (!w || !qw || !sw)) return FP8BS_ERR_NULL;
+  if (M > 0 && (!ld_ok(ldx, K) || !ld_ok(ldq, K) || lds < M || !aligned(x, 16) ||
+                !aligned(q, 16) || !aligned(s, 4)))
+    return FP8BS_ERR_LAYOUT;
+  if (N > 0 && (!ld_ok(ldw, K) || !ld_ok(ldqw, K) || !aligned(w, 16) || !aligned(qw, 16) ||
+                !aligned(sw, 4)))
+    return FP8BS_ERR_LAYOUT;
+  return hip_status(fp8bs::launch_quant_linear(x, M, K, ldx, q, ldq, s, lds, w, N, ldw, qw,
+                                               ldqw, sw, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_quant_act_128x1_t(const uint16_t* x, int64_t M, int64_t N, int64_t ldx, uint8_t* qt,
                           int64_t ldqt, float* st, int64_t ldst, void* stream) {
   if (M < 0 || N < 0 || M % kTile != 0 || N % kTile != 0) return FP8BS_ERR_SHAPE;

@@ -48,6 +48,12 @@ hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                           uint8_t* q, int64_t ldq, float* s, uint8_t* qt, int64_t ldqt,
                           float* st, hipStream_t stream);
 
+// launch_quant_act and launch_quant_w (no transposed output) in one launch
+hipError_t launch_quant_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                               const uint16_t* w, int64_t N, int64_t ldw, uint8_t* qw,
+                               int64_t ldqw, float* sw, hipStream_t stream);
+
 // Output element type of the GEMM kernels.
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2 };
 

@@ -19,12 +19,33 @@ namespace {
 constexpr int kActRowsPerWG = 64;   // rows of one 1x128 column of tiles per workgroup
 constexpr int kActIters = kActRowsPerWG / 16;
 
-// grid: one workgroup per (64-row band, K group), K group fastest so that
-// consecutive workgroups walk along the same rows.
-__global__ __launch_bounds__(256) void quant_act_1x128_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t KB, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds) {
-  const int64_t bid = blockIdx.x;
+struct ActArgs {
+  const uint16_t* x;
+  int64_t M, KB, ldx;
+  uint8_t* q;
+  int64_t ldq;
+  float* s;
+  int64_t lds;
+};
+
+struct WArgs {
+  const uint16_t* w;
+  int64_t N, KB, ldw;
+  uint8_t* q;
+  int64_t ldq;
+  float* s;
+  uint8_t* qt;
+  int64_t ldqt;
+  float* st;
+};
+
+// Work item `bid` of the activation quantizer: one (64-row band, K group),
+// K group fastest so that consecutive workgroups walk along the same rows.
+__device__ __forceinline__ void act_band(const ActArgs& a, int64_t bid) {
+  const uint16_t* __restrict__ x = a.x;
+  uint8_t* __restrict__ q = a.q;
+  float* __restrict__ s = a.s;
+  const int64_t M = a.M, KB = a.KB, ldx = a.ldx, ldq = a.ldq, lds = a.lds;
   const int64_t kb = bid % KB;
   const int64_t m0 = (bid / KB) * kActRowsPerWG;
   const int lane = threadIdx.x & 15;
@@ -50,6 +71,10 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
       if (lane == 0) s[kb * lds + m] = sc;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(ActArgs a) {
+  act_band(a, blockIdx.x);
 }
 
 // Transpose of an 8x8 byte block: row i is (lo[i], hi[i]) (bytes 0..3, 4..7);
@@ -79,14 +104,16 @@ __device__ __forceinline__ void transpose8x8(const uint32_t (&lo)[8], const uint
 // thread then reads an 8x8 byte block, transposes it in registers and writes
 // eight 8-byte row pieces of qt.
 template <bool TRANS>
-__global__ __launch_bounds__(256) void quant_w_128x128_kernel(
-    const uint16_t* __restrict__ w, int64_t N, int64_t KB, int64_t ldw,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, uint8_t* __restrict__ qt,
-    int64_t ldqt, float* __restrict__ st) {
+__device__ __forceinline__ void w_block(const WArgs& a, int64_t bid) {
+  const uint16_t* __restrict__ w = a.w;
+  uint8_t* __restrict__ q = a.q;
+  float* __restrict__ s = a.s;
+  uint8_t* __restrict__ qt = a.qt;
+  float* __restrict__ st = a.st;
+  const int64_t N = a.N, KB = a.KB, ldw = a.ldw, ldq = a.ldq, ldqt = a.ldqt;
   __shared__ float wave_max[4];
   constexpr int kPitch = 136;  // LDS row pitch of the staged codes (bytes)
   __shared__ __attribute__((aligned(16))) uint8_t tile[TRANS ? 128 * kPitch : 8];
-  const int64_t bid = blockIdx.x;
   const int64_t kb = bid % KB;
   const int64_t nb = bid / KB;
   const int lane = threadIdx.x & 15;
@@ -141,6 +168,24 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(
                                   reinterpret_cast<u32x2*>(qt + k * ldqt + nb * 128 + n0));
     }
     if (threadIdx.x == 0) st[kb * NB + nb] = sc;
+  }
+}
+
+template <bool TRANS>
+__global__ __launch_bounds__(256) void quant_w_128x128_kernel(WArgs a) {
+  w_block<TRANS>(a, blockIdx.x);
+}
+
+// Both operands of a forward linear layer in one launch: workgroups
+// [0, w_blocks) quantize the weight's 128x128 blocks, the rest the
+// activation's 1x128 tiles.  The activation's short stream then fills the
+// end of the weight stream instead of paying its own launch ramp and drain.
+__global__ __launch_bounds__(256) void quant_linear_kernel(ActArgs a, WArgs w, int64_t w_blocks) {
+  const int64_t bid = blockIdx.x;
+  if (bid < w_blocks) {
+    w_block<false>(w, bid);
+  } else {
+    act_band(a, bid - w_blocks);
   }
 }
 
@@ -256,7 +301,7 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   const int64_t blocks = MB * KB;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     x, M, KB, ldx, q, ldq, s, lds);
+                     ActArgs{x, M, KB, ldx, q, ldq, s, lds});
   return hipGetLastError();
 }
 
@@ -267,13 +312,30 @@ hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
   const int64_t NB = (N + 127) / 128;
   const int64_t blocks = NB * KB;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const WArgs a{w, N, KB, ldw, q, ldq, s, qt, ldqt, st};
   if (qt) {
     hipLaunchKernelGGL(quant_w_128x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, w, N, KB, ldw, q, ldq, s, qt, ldqt, st);
+                       stream, a);
   } else {
     hipLaunchKernelGGL(quant_w_128x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, w, N, KB, ldw, q, ldq, s, qt, ldqt, st);
+                       stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                               const uint16_t* w, int64_t N, int64_t ldw, uint8_t* qw,
+                               int64_t ldqw, float* sw, hipStream_t stream) {
+  const int64_t KB = K / 128;
+  const int64_t w_blocks = (N + 127) / 128 * KB;
+  const int64_t a_blocks = (M + kActRowsPerWG - 1) / kActRowsPerWG * KB;
+  const int64_t blocks = w_blocks + a_blocks;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_linear_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     ActArgs{x, M, KB, ldx, q, ldq, s, lds},
+                     WArgs{w, N, KB, ldw, qw, ldqw, sw, nullptr, 0, nullptr}, w_blocks);
   return hipGetLastError();
 }
 

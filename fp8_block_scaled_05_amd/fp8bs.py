@@ -26,6 +26,7 @@ EXPORTS = (
     "fp8_quant_act_128x1_t",
     "fp8_quant_w_128x128",
     "fp8_quant_w_128x128_t",
+    "fp8_quant_linear",
     "fp8_block_gemm",
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_e4m3_out",
@@ -49,6 +50,8 @@ _SIGNATURES = {
     "fp8_quant_w_128x128": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p], _int),
     "fp8_quant_w_128x128_t": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p], _int),
     "fp8_quant_act_128x1_t": ([_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _int),
+    "fp8_quant_linear": ([_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
+                          _p, _p], _int),
     "fp8_block_gemm_rowscaled": ([_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _int, _i64,
                                   _i64, _i64, _p], _int),
     "fp8_block_kgrouped_gemm_rowscaled": ([_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64,
@@ -194,6 +197,32 @@ def fp8_quant_w_128x128(w, q=None, s=None):
     _check(lib.fp8_quant_w_128x128(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _stream(w)),
            "fp8_quant_w_128x128")
     return q, s
+
+
+def fp8_quant_linear(x, w, q=None, s=None, qw=None, sw=None):
+    """Both operands of y = x . W^T in one launch: returns ``(q, s, qw, sw)``,
+    exactly ``fp8_quant_act_1x128(x)`` and ``fp8_quant_w_128x128(w)``."""
+    _need_device(x, w, q, s, qw, sw)
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("x and w must be bfloat16")
+    M, K = x.shape
+    N, Kw = w.shape
+    if Kw != K:
+        raise ValueError(f"x has K={K} columns but w has {Kw}")
+    ldx = _rowmajor(x, "x") if M else K
+    ldw = _rowmajor(w, "w") if N else K
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(K // 128, M, dtype=torch.float32, device=x.device)
+    if qw is None:
+        qw = torch.empty(N, K, dtype=torch.uint8, device=w.device)
+    if sw is None:
+        sw = torch.empty((N + 127) // 128, K // 128, dtype=torch.float32, device=w.device)
+    _check(lib.fp8_quant_linear(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), s.shape[1],
+                                _ptr(w), N, ldw, _ptr(qw), _ld(qw), _ptr(sw), _stream(x)),
+           "fp8_quant_linear")
+    return q, s, qw, sw
 
 
 def fp8_quant_w_128x128_t(w, q=None, s=None, qt=None, st=None):

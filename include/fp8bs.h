@@ -160,6 +160,27 @@ int fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                         uint8_t* q, int64_t ldq, float* s, void* stream);
 
 /*
+ * Both operands of a forward linear layer, y = x . W^T, quantized in one
+ * launch: exactly fp8_quant_act_1x128 on x and fp8_quant_w_128x128 on W
+ * (same codes, scales and layouts), with one launch's ramp and drain instead
+ * of two.  Pages: as those two calls (the activation and the weight are both
+ * quantized online, on every step).
+ *
+ *   x, q, s, ldx, ldq, lds  as fp8_quant_act_1x128 (M rows).
+ *   w, qw, sw, ldw, ldqw    as fp8_quant_w_128x128's w, q, s, ldw, ldq
+ *                           (N rows).
+ *   K is shared.  M == 0 or N == 0 skips that operand (its pointers are not
+ *   read); both zero launches nothing.
+ * Errors: K not a positive multiple of 128, M < 0 or N < 0 -> ERR_SHAPE;
+ *         a NULL pointer of a non-empty operand -> ERR_NULL; that operand's
+ *         layout or alignment as in the single calls -> ERR_LAYOUT.
+ */
+int fp8_quant_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                     uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                     const uint16_t* w, int64_t N, int64_t ldw, uint8_t* qw,
+                     int64_t ldqw, float* sw, void* stream);
+
+/*
  * Quantization in groups of 128 consecutive rows per column, with the codes
  * written transposed: the operands of the weight-gradient GEMM
  * dW[N][K] = dY^T . X of the backward pass, which contracts over the M

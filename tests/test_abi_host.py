@@ -78,6 +78,25 @@ def test_quant_act_validation(fp8bs):
     assert _qa(lib, s=P + 2) == fp8bs.ERR_LAYOUT
 
 
+def test_quant_linear_validation(fp8bs):
+    lib = fp8bs.lib
+
+    def ql(x=P, M=64, K=256, ldx=256, q=P, ldq=256, s=P, lds=64, w=P, N=128, ldw=256, qw=P,
+           ldqw=256, sw=P):
+        return lib.fp8_quant_linear(x, M, K, ldx, q, ldq, s, lds, w, N, ldw, qw, ldqw, sw, None)
+
+    assert ql(K=100) == fp8bs.ERR_SHAPE
+    assert ql(M=-1) == fp8bs.ERR_SHAPE
+    assert ql(N=-1) == fp8bs.ERR_SHAPE
+    assert ql(M=0, N=0, x=0, w=0) == fp8bs.OK
+    assert ql(x=0) == fp8bs.ERR_NULL
+    assert ql(sw=0) == fp8bs.ERR_NULL
+    assert ql(lds=32) == fp8bs.ERR_LAYOUT
+    assert ql(ldqw=200) == fp8bs.ERR_LAYOUT
+    assert ql(w=P + 8) == fp8bs.ERR_LAYOUT
+    assert ql(x=P + 2) == fp8bs.ERR_LAYOUT
+
+
 def test_quant_w_validation(fp8bs):
     lib = fp8bs.lib
     f = lambda w=P, N=256, K=256, ldw=256, q=P, ldq=256, s=P: lib.fp8_quant_w_128x128(

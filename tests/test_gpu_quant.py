@@ -139,3 +139,43 @@ def test_full_size_weight_18432x7168_sampled_bands(fp8bs):
         qr, sr = oracle.quant_w_128x128(wb[nb * 128:(nb + 1) * 128])
         gu.assert_same_bits(qh[nb * 128:(nb + 1) * 128], qr, f"band {nb} codes")
         gu.assert_same_bits(sh[nb:nb + 1], sr, f"band {nb} scales")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (63, 300, 384), (1000, 130, 1024),
+                                   (0, 200, 256), (77, 0, 256)])
+def test_linear_pair_equals_oracle(fp8bs, M, N, K):
+    """One launch for both operands gives the oracle's codes and scales for
+    each, on ragged row counts and with either operand empty."""
+    xb = synth.bf16_bits(synth.act(M, K, case=400 + M, tensor=0))
+    wb = synth.bf16_bits(synth.weight(N, K, case=400 + N, tensor=1))
+    q, s, qw, sw = fp8bs.fp8_quant_linear(gu.bf16_from_bits(xb), gu.bf16_from_bits(wb))
+    torch.cuda.synchronize()
+    if M:
+        qr, sr = oracle.quant_act_1x128(xb)
+        gu.assert_same_bits(gu.host(q), qr, "act codes")
+        gu.assert_same_bits(gu.host(s), sr, "act scales")
+    if N:
+        qr, sr = oracle.quant_w_128x128(wb)
+        gu.assert_same_bits(gu.host(qw), qr, "weight codes")
+        gu.assert_same_bits(gu.host(sw), sr, "weight scales")
+
+
+def test_linear_pair_full_size_equals_single_calls(fp8bs):
+    """The dense layer's operands (4096x7168 activation, 18432x7168 weight):
+    the one-launch pair is bitwise the two single calls, and sampled rows and
+    bands equal the oracle."""
+    x = synth.act(4096, 7168, case=synth.DENSE.case_id, tensor=0, device="cuda")
+    w = synth.weight(18432, 7168, case=synth.DENSE.case_id, tensor=1, device="cuda")
+    q, s, qw, sw = fp8bs.fp8_quant_linear(x, w)
+    q1, s1 = fp8bs.fp8_quant_act_1x128(x)
+    qw1, sw1 = fp8bs.fp8_quant_w_128x128(w)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q1) and torch.equal(s.view(torch.int32), s1.view(torch.int32))
+    assert torch.equal(qw, qw1) and torch.equal(sw.view(torch.int32), sw1.view(torch.int32))
+    xb, wb = synth.bf16_bits(x[:256]), synth.bf16_bits(w[-256:])
+    qr, sr = oracle.quant_act_1x128(xb)
+    gu.assert_same_bits(gu.host(q[:256]), qr, "act codes, first rows")
+    gu.assert_same_bits(gu.host(s[:, :256]), sr, "act scales, first rows")
+    qr, sr = oracle.quant_w_128x128(wb)
+    gu.assert_same_bits(gu.host(qw[-256:]), qr, "weight codes, last bands")
+    gu.assert_same_bits(gu.host(sw[-2:]), sr, "weight scales, last bands")
