@@ -165,6 +165,17 @@ __device__ __forceinline__ void dense_tile(const GemmArgs& p, int64_t i, TileCoo
   t.c = p.c;
 }
 
+// Range [lo, hi) of group g from the device offsets, clamped to [0, limit]
+// and to hi >= lo: offsets that break the documented contract then give
+// unspecified results but no access outside the operands.
+__device__ __forceinline__ void group_range(const GemmArgs& p, int64_t g, int64_t limit,
+                                            int64_t& lo, int64_t& hi) {
+  lo = p.group_offsets[g];
+  hi = p.group_offsets[g + 1];
+  lo = lo < 0 ? 0 : (lo > limit ? limit : lo);
+  hi = hi < lo ? lo : (hi > limit ? limit : hi);
+}
+
 // Grouped along K: group g owns the K range [off[g], off[g+1]) (multiples of
 // 128) and its own output C_g = c + g * c_group_stride; every group has the
 // same MT x NT tiles, walked group after group.  KB == 0 for an empty group.
@@ -180,9 +191,10 @@ __device__ __forceinline__ void kgrouped_tile(const GemmArgs& p, int64_t i, Tile
   t.sb = p.sb;
   t.row0 = tm * C::BM;
   t.row_end = p.M;
-  const int64_t o0 = p.group_offsets[g], o1 = p.group_offsets[g + 1];
+  int64_t o0, o1;
+  group_range(p, g, p.K / 128 * 128, o0, o1);
   t.kb0 = o0 / 128;
-  t.KB = (o1 - o0) / 128;
+  t.KB = o1 / 128 - t.kb0;
   t.c = static_cast<char*>(p.c) + g * p.c_group_stride * out_bytes;
 }
 
@@ -202,7 +214,10 @@ __device__ __forceinline__ int wave_incl_sum(int v) {
 // of the workgroup computes the same, uniform, result).
 template <class C>
 __device__ __forceinline__ int group_row_tiles(const GemmArgs& p, int64_t g) {
-  return g < p.G ? (p.group_offsets[g + 1] - p.group_offsets[g] + C::BM - 1) / C::BM : 0;
+  if (g >= p.G) return 0;
+  int64_t lo, hi;
+  group_range(p, g, p.M, lo, hi);
+  return (int)((hi - lo + C::BM - 1) / C::BM);
 }
 
 // Total tile-rows over all groups.
@@ -238,8 +253,10 @@ __device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t i, int64
     }
     seen += chunk;
   }
-  t.row0 = p.group_offsets[g] + local * C::BM;
-  t.row_end = p.group_offsets[g + 1];
+  int64_t lo, hi;
+  group_range(p, g, p.M, lo, hi);
+  t.row0 = lo + local * C::BM;
+  t.row_end = hi;
   t.b = p.b + g * p.b_group_stride;
   t.sb = p.sb + g * NB * p.sb_ld;
   t.kb0 = 0;

@@ -347,6 +347,8 @@ def fp8_block_grouped_gemm(a, sa, b, sb, group_offsets, out=None, out_dtype=torc
         raise ValueError("group_offsets must be int32")
     M_total, K = a.shape
     G, N, _ = b.shape
+    if group_offsets.numel() != G + 1:
+        raise ValueError(f"group_offsets must hold G + 1 = {G + 1} entries")
     if out is None:
         out = torch.empty(M_total, N, dtype=out_dtype, device=a.device)
     _check(lib.fp8_block_grouped_gemm(_ptr(a), _ld(a), _ptr(sa), sa.shape[1], _ptr(b),
@@ -402,6 +404,8 @@ def fp8_block_grouped_gemm_e4m3_out(a, sa, b, sb, group_offsets, qc=None, sc=Non
         raise ValueError("group_offsets must be int32")
     M_total, K = a.shape
     G, N, _ = b.shape
+    if group_offsets.numel() != G + 1:
+        raise ValueError(f"group_offsets must hold G + 1 = {G + 1} entries")
     qc, sc = _e4m3_outputs(M_total, N, qc, sc, a.device)
     _check(lib.fp8_block_grouped_gemm_e4m3_out(_ptr(a), _ld(a), _ptr(sa), sa.shape[1], _ptr(b),
                                                b.stride(1), b.stride(0), _ptr(sb), _ptr(qc),

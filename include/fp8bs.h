@@ -321,7 +321,11 @@ int fp8_block_gemm_rowscaled(const uint8_t* a, int64_t lda, const float* sa,
  *           ldc; fp32 or bf16 by out_kind.  An expert without tokens gets
  *           C_g = 0.
  *   group_offsets DEVICE int32 [G+1], 0 = off[0] <= ... <= off[G] = K_total,
- *           every offset a multiple of 128.  Trusted, not validated.
+ *           every offset a multiple of 128.  Not validated (read on the
+ *           device): each range is clamped to [0, K_total] with its end at
+ *           least its start, and an offset that is not a multiple of 128 is
+ *           rounded down; results for such offsets are unspecified but no
+ *           access leaves the operands.
  * Errors: as fp8_block_gemm_rowscaled; G outside [1, 4096] or K_total not a
  *         multiple of 128 -> ERR_SHAPE; c_group_stride < (M-1)*ldc + N ->
  *         ERR_LAYOUT.
@@ -349,8 +353,11 @@ int fp8_block_kgrouped_gemm_rowscaled(const uint8_t* a, int64_t lda,
  *                 sb[(g*ceil(N/128) + nb)*(K/128) + kb].
  *   group_offsets DEVICE int32 [G+1], 0 = off[0] <= off[1] <= ... <=
  *                 off[G] = M_total.  Read on the device (no host
- *                 synchronisation); trusted, not validated.  Empty groups are
- *                 allowed and write nothing.
+ *                 synchronisation), so not validated: the kernel clamps each
+ *                 group's range to [0, M_total] (and its end to at least its
+ *                 start), so offsets outside this contract give unspecified
+ *                 results but no access outside the operands.  Empty groups
+ *                 are allowed and write nothing.
  * Errors: as above; G < 1 or G > 4096 -> ERR_SHAPE.
  */
 int fp8_block_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa,

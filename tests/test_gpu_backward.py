@@ -316,3 +316,26 @@ def test_kgrouped_weight_gradient(fp8bs, sizes, M, N, out, gpu_quant):
             assert np.all(dwh[g] == 0.0), f"expert {g} without tokens must be zero"
         else:
             gu.check_gemm(dwh[g], C[g], B[g], bf16=out == torch.bfloat16)
+
+
+def test_kgrouped_offsets_outside_the_contract_stay_in_bounds(fp8bs):
+    """Expert ranges out of order and past the end are clamped on the device:
+    expert 0 over tokens [0, 256), expert 1 empty (its end 128 is raised to
+    its start 256), expert 2 over [128, T) (its end T + 128 is lowered to T).
+    Each expert has its own output, so every result stays defined."""
+    M, N = 256, 128
+    dy, x, _ = _token_groups([384], M, N, case=890)
+    T = dy.shape[0]
+    qa_o, sa_o = oracle.quant_act_128x1_t(synth.bf16_bits(dy))
+    qb_o, sb_o = oracle.quant_act_128x1_t(synth.bf16_bits(x))
+    offsets = np.array([0, 256, 128, T + 128], dtype=np.int32)
+    dw = torch.full((3, M, N), 5.0, dtype=torch.float32, device="cuda")
+    fp8bs.fp8_block_kgrouped_gemm_rowscaled(gu.u8(qa_o), gu.f32(sa_o), gu.u8(qb_o), gu.f32(sb_o),
+                                            torch.from_numpy(offsets).cuda(), out=dw)
+    torch.cuda.synchronize()
+    dwh = gu.host_f64(dw)
+    C0, B0 = oracle.block_gemm_rowscaled(qa_o[:, :256], sa_o[:2], qb_o[:, :256], sb_o[:2])
+    gu.check_gemm(dwh[0], C0, B0)
+    assert np.all(dwh[1] == 0.0)
+    C2, B2 = oracle.block_gemm_rowscaled(qa_o[:, 128:T], sa_o[1:], qb_o[:, 128:T], sb_o[1:])
+    gu.check_gemm(dwh[2], C2, B2)

@@ -156,3 +156,30 @@ def test_last_round_split_all_outputs(fp8bs):
     c = _run(fp8bs, qa, sa, qw, sw, offsets, torch.float32)
     C, B = oracle.block_grouped_gemm(qa, sa, qw, sw, offsets)
     gu.check_gemm(c, C, B)
+
+
+def test_offsets_outside_the_contract_stay_in_bounds(fp8bs):
+    """Decreasing offsets and a last offset past M_total: the kernel clamps
+    each group's range to [0, M_total] (end >= start), so nothing is read or
+    written outside the operands.  Rows covered by one group only keep
+    defined results: rows 0..99 (expert 0 only) and 500..M-1 (expert 3,
+    whose end is clamped to M)."""
+    M, N, K = 640, 256, 384
+    offsets = np.array([0, 300, 100, 500, M + 50], dtype=np.int32)
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(synth.act(M, K, case=515, tensor=0)))
+    qw, sw = _experts(4, N, K, 515)
+    c = gu.host_f64(_run(fp8bs, qa, sa, qw, sw, offsets, torch.float32))
+    C0, B0 = oracle.block_gemm(qa[:100], sa[:, :100], qw[0], sw[0])
+    gu.check_gemm(c[:100], C0, B0)
+    C3, B3 = oracle.block_gemm(qa[500:], sa[:, 500:], qw[3], sw[3])
+    gu.check_gemm(c[500:], C3, B3)
+
+
+def test_binding_checks_offset_count(fp8bs):
+    qa = torch.zeros(64, 128, dtype=torch.uint8, device="cuda")
+    sa = torch.ones(1, 64, dtype=torch.float32, device="cuda")
+    qw = torch.zeros(3, 128, 128, dtype=torch.uint8, device="cuda")
+    sw = torch.ones(3, 1, 1, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        fp8bs.fp8_block_grouped_gemm(qa, sa, qw, sw,
+                                     torch.tensor([0, 64], dtype=torch.int32, device="cuda"))
