@@ -290,3 +290,59 @@ def test_binding_refuses_cpu_tensors(fp8bs):
     import torch
     with pytest.raises(ValueError):
         fp8bs.fp8_quant_act_1x128(torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+def test_binding_checks_tensor_shapes_before_the_call(fp8bs):
+    """The library receives pointers and row strides only, so the binding
+    checks every tensor's extent and dtype first (these CPU tensors never
+    reach the library: the device check comes after the shape checks)."""
+    import torch
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    x = torch.zeros(4, 256, dtype=bf)
+    with pytest.raises(ValueError, match="q must be a 2-D tensor of at least"):
+        fp8bs.fp8_quant_act_1x128(x, q=torch.zeros(4, 128, dtype=u8))
+    with pytest.raises(ValueError, match="s must be a 2-D tensor of at least"):
+        fp8bs.fp8_quant_act_1x128(x, s=torch.zeros(2, 3, dtype=f32))
+    with pytest.raises(ValueError, match="K = 100"):
+        fp8bs.fp8_quant_act_1x128(torch.zeros(4, 100, dtype=bf))
+    with pytest.raises(ValueError, match="row stride 2"):
+        fp8bs.fp8_quant_w_128x128(torch.zeros(200, 256, dtype=bf),
+                                  s=torch.zeros(2, 4, dtype=f32)[:, :2])
+    a, sa = torch.zeros(64, 256, dtype=u8), torch.zeros(2, 64, dtype=f32)
+    b, sb = torch.zeros(300, 256, dtype=u8), torch.zeros(3, 2, dtype=f32)
+    with pytest.raises(ValueError, match="sa must be a 2-D tensor of at least"):
+        fp8bs.fp8_block_gemm(a, sa[:, :32], b, sb)
+    with pytest.raises(ValueError, match="sb must be a 2-D tensor of at least"):
+        fp8bs.fp8_block_gemm(a, sa, b, sb[:2])
+    with pytest.raises(ValueError, match="b must be a 2-D tensor of at least"):
+        fp8bs.fp8_block_gemm(a, sa, b[:, :128], sb)
+    with pytest.raises(ValueError, match="E4M3 codes need their scales"):
+        fp8bs.fp8_block_gemm(a, None, b, sb)
+    with pytest.raises(ValueError, match="out must be a 2-D tensor of at least"):
+        fp8bs.fp8_block_gemm(a, sa, b, sb, out=torch.zeros(64, 256, dtype=bf))
+    with pytest.raises(ValueError, match="a must be uint8"):
+        fp8bs.fp8_block_gemm(a.float(), sa, b, sb)
+    with pytest.raises(ValueError, match="multiple of 128"):
+        fp8bs.fp8_block_gemm_e4m3_out(a, sa, b, sb)
+    bg, sbg = torch.zeros(2, 128, 256, dtype=u8), torch.zeros(2, 1, 2, dtype=f32)
+    off = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="sb must be a contiguous"):
+        fp8bs.fp8_block_grouped_gemm(a, sa, bg, sbg[:, :, :1], off)
+    with pytest.raises(ValueError, match="G \\+ 1 = 3"):
+        fp8bs.fp8_block_grouped_gemm(a, sa, bg, sbg, off[:2])
+    with pytest.raises(ValueError, match="per-tile history"):
+        fp8bs.fp8_quant_act_1x128_delayed(x, torch.zeros(4, 2, 3), 0, "tile")
+    # well-formed CPU arguments pass every check and stop at the device check
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        fp8bs.fp8_block_gemm(a, sa, b, sb)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        fp8bs.fp8_block_grouped_gemm(a, sa, bg, sbg, off)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        fp8bs.fp8_quant_linear(x, torch.zeros(130, 256, dtype=bf))
+
+
+def test_binding_accepts_empty_operands_with_any_strides(fp8bs):
+    import torch
+    x = torch.zeros(256, 0, dtype=torch.bfloat16).t()  # [0][256], column stride 256
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        fp8bs.fp8_quant_linear(x, torch.zeros(130, 256, dtype=torch.bfloat16))
