@@ -188,8 +188,6 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
     out["act_quant_8192x7168"] = {"us": ms * 1e3, "GBps": byt / ms / 1e6,
                                   "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
                                   "bytes": byt}
-    del xs, qs, ss
-    torch.cuda.empty_cache()
 
     # weight quantizer 18432x7168, 2 rotated sets (793 MB)
     ws = [synth.weight(N, K, case=synth.QUANT.case_id, tensor=10 + i, device="cuda") for i in range(2)]
@@ -203,6 +201,20 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
     byt = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
     out["weight_quant_18432x7168"] = {"us": ms * 1e3, "GBps": byt / ms / 1e6,
                                       "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS, "bytes": byt}
+
+    # the quantizer workload as a whole: the 8192x7168 activation and the
+    # 18432x7168 weight in one launch, 2 rotated sets (1.15 GB)
+    for i in range(iters + 5):
+        j = i % 2
+        f = lambda: fp8bs.fp8_quant_linear(xs[j], ws[j], qs[j], ss[j], qws[j], sws[j])
+        (tm.run("qpair", f) if i >= 5 else f())
+    ms = tm.med_ms("qpair")
+    byt = Mq * Kq * 3.03125 + byt
+    out["quant_pair_8192x7168_and_18432x7168"] = {
+        "us": ms * 1e3, "GBps": byt / ms / 1e6, "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
+        "bytes": byt}
+    del xs, qs, ss
+    torch.cuda.empty_cache()
 
     # skinny GEMM with in-call activation quantization, W rotated over 4 copies
     wq = [(qws[i % 2].clone(), sws[i % 2].clone()) for i in range(4)]
