@@ -13,8 +13,9 @@
 //               t % H (the tile has one owner, so no race);
 //   per tensor: ring hist[H + 2], step u in slot u % (H + 2); every workgroup
 //               reads the H window slots, raises slot t % (H + 2) to its
-//               maximum with an atomic max, and clears slot (t + 1) % (H + 2)
-//               for the next step (no slot is both read and written).  The
+//               maximum with an atomic max, and workgroup 0 clears slot
+//               (t + 1) % (H + 2) for the next step (no slot is both read and
+//               written).  The
 //               atomics of all workgroups meet at one address, so a
 //               workgroup first reads the slot and skips the atomic when its
 //               maximum cannot raise it (the slot only grows during a step).
@@ -94,8 +95,13 @@ __global__ __launch_bounds__(256) void quant_act_delayed_kernel(DelayArgs a) {
   const int64_t ring = TENSOR ? a.H + 2 : a.H;
   float win_tensor = 0.0f;
   if constexpr (TENSOR) {
-    for (int64_t d = 0; d < a.H; ++d)
-      win_tensor = fmaxf(win_tensor, a.hist[((a.step - 1 - d) % ring + ring) % ring]);
+    // the window's H slots, 64 at a time across the wave's lanes
+    const int l64 = threadIdx.x & 63;
+    for (int64_t h0 = 0; h0 < a.H; h0 += 64) {
+      const int64_t d = h0 + l64;
+      if (d < a.H) win_tensor = fmaxf(win_tensor, a.hist[((a.step - 1 - d) % ring + ring) % ring]);
+    }
+    win_tensor = max_wave64(win_tensor);
   }
   uint32_t clipped = 0, flushed = 0;
   float tmax = 0.0f;
@@ -138,7 +144,10 @@ __global__ __launch_bounds__(256) void quant_act_delayed_kernel(DelayArgs a) {
       unsigned int* const slot = reinterpret_cast<unsigned int*>(a.hist + a.step % ring);
       if (__float_as_uint(wmax) > __atomic_load_n(slot, __ATOMIC_RELAXED))
         atomicMax(slot, __float_as_uint(wmax));
-      a.hist[(a.step + 1) % ring] = 0.0f;
+      // one workgroup clears the next step's slot (the next call is ordered
+      // after this one on its stream); a store from every workgroup to one
+      // address would serialize them
+      if (bid == 0) a.hist[(a.step + 1) % ring] = 0.0f;
     }
   }
   if (a.stats) {
