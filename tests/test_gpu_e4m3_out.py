@@ -263,3 +263,25 @@ def test_grouped_many_groups(fp8bs):
         C, B, qc_ref, _ = oracle.block_gemm_e4m3_out(qa[r0:r1], sa[:, r0:r1], qw[g], sw[g])
         check_e4m3_out(qc_h[r0:r1], sc_h[:, r0:r1], C, B, C_codes=qc_ref,
                        min_equal=0.99 if r1 - r0 > 20 else 0.9)
+
+
+def test_usage_flow_of_the_readme(fp8bs):
+    """The calls the README shows, at a small size: both operands quantized
+    in one launch, the bf16 GEMM, and the GEMM with E4M3 output, against the
+    oracle."""
+    x = synth.act(256, 384, case=640, tensor=0, device="cuda")
+    w = synth.weight(512, 384, case=640, tensor=1, device="cuda")
+    qa, sa, qw, sw = fp8bs.fp8_quant_linear(x, w)
+    y = fp8bs.fp8_block_gemm(qa, sa, qw, sw)
+    q_next, s_next = fp8bs.fp8_block_gemm_e4m3_out(qa, sa, qw, sw)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16 and tuple(y.shape) == (256, 512)
+    qr, sr = oracle.quant_act_1x128(synth.bf16_bits(x))
+    qwr, swr = oracle.quant_w_128x128(synth.bf16_bits(w))
+    gu.assert_same_bits(gu.host(qa), qr, "activation codes")
+    gu.assert_same_bits(gu.host(sa), sr, "activation scales")
+    gu.assert_same_bits(gu.host(qw), qwr, "weight codes")
+    gu.assert_same_bits(gu.host(sw), swr, "weight scales")
+    C, B, qc_ref, _ = oracle.block_gemm_e4m3_out(qr, sr, qwr, swr)
+    gu.check_gemm(y, C, B)
+    check_e4m3_out(gu.host(q_next), gu.host(s_next), C, B, C_codes=qc_ref)
