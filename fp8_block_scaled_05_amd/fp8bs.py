@@ -109,9 +109,16 @@ def _ptr(t):
 
 
 def _need_device(*ts):
+    devices = set()
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("libfp8bs works on GPU tensors only")
+        devices.add(t.device)
+    if len(devices) > 1:
+        raise ValueError("all tensors of a call must be on one GPU, got "
+                         f"{sorted(map(str, devices))}")
 
 
 def _mat(t, name, rows, cols, dtype, ld=None):
@@ -180,8 +187,9 @@ def fp8_quant_act_1x128(x, q=None, s=None, lds=None):
         q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty(KB, lds or M, dtype=torch.float32, device=x.device)
-    _check(lib.fp8_quant_act_1x128(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), s.stride(0),
-                                   _stream(x)), "fp8_quant_act_1x128")
+    with torch.cuda.device(x.device):
+        _check(lib.fp8_quant_act_1x128(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), s.stride(0),
+                                       _stream(x)), "fp8_quant_act_1x128")
     return q, s
 
 
@@ -220,9 +228,11 @@ def fp8_quant_act_1x128_delayed(x, hist, step, mode="tile", q=None, s=None, stat
         q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty(KB, M, dtype=torch.float32, device=x.device)
-    _check(lib.fp8_quant_act_1x128_delayed(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s),
-                                           s.stride(0), m, _ptr(hist), ldh, H, step, _ptr(stats),
-                                           _stream(x)), "fp8_quant_act_1x128_delayed")
+    with torch.cuda.device(x.device):
+        _check(lib.fp8_quant_act_1x128_delayed(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s),
+                                               s.stride(0), m, _ptr(hist), ldh, H, step,
+                                               _ptr(stats), _stream(x)),
+               "fp8_quant_act_1x128_delayed")
     return q, s
 
 
@@ -239,8 +249,9 @@ def fp8_quant_w_128x128(w, q=None, s=None):
         q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
     if s is None:
         s = torch.empty((N + 127) // 128, KB, dtype=torch.float32, device=w.device)
-    _check(lib.fp8_quant_w_128x128(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _stream(w)),
-           "fp8_quant_w_128x128")
+    with torch.cuda.device(w.device):
+        _check(lib.fp8_quant_w_128x128(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _stream(w)),
+               "fp8_quant_w_128x128")
     return q, s
 
 
@@ -269,9 +280,10 @@ def fp8_quant_linear(x, w, q=None, s=None, qw=None, sw=None):
         qw = torch.empty(N, K, dtype=torch.uint8, device=w.device)
     if sw is None:
         sw = torch.empty((N + 127) // 128, KB, dtype=torch.float32, device=w.device)
-    _check(lib.fp8_quant_linear(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), s.stride(0),
-                                _ptr(w), N, ldw, _ptr(qw), _ld(qw), _ptr(sw), _stream(x)),
-           "fp8_quant_linear")
+    with torch.cuda.device(x.device):
+        _check(lib.fp8_quant_linear(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), s.stride(0),
+                                    _ptr(w), N, ldw, _ptr(qw), _ld(qw), _ptr(sw), _stream(x)),
+               "fp8_quant_linear")
     return q, s, qw, sw
 
 
@@ -296,8 +308,9 @@ def fp8_quant_w_128x128_t(w, q=None, s=None, qt=None, st=None):
     s = torch.empty(NB, KB, dtype=torch.float32, device=dev) if s is None else s
     qt = torch.empty(K, N, dtype=torch.uint8, device=dev) if qt is None else qt
     st = torch.empty(KB, NB, dtype=torch.float32, device=dev) if st is None else st
-    _check(lib.fp8_quant_w_128x128_t(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _ptr(qt),
-                                     _ld(qt), _ptr(st), _stream(w)), "fp8_quant_w_128x128_t")
+    with torch.cuda.device(w.device):
+        _check(lib.fp8_quant_w_128x128_t(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _ptr(qt),
+                                         _ld(qt), _ptr(st), _stream(w)), "fp8_quant_w_128x128_t")
     return q, s, qt, st
 
 
@@ -317,8 +330,9 @@ def fp8_quant_act_128x1_t(x, qt=None, st=None):
         qt = torch.empty(N, M, dtype=torch.uint8, device=x.device)
     if st is None:
         st = torch.empty(M // 128, N, dtype=torch.float32, device=x.device)
-    _check(lib.fp8_quant_act_128x1_t(_ptr(x), M, N, ldx, _ptr(qt), _ld(qt), _ptr(st),
-                                     st.stride(0), _stream(x)), "fp8_quant_act_128x1_t")
+    with torch.cuda.device(x.device):
+        _check(lib.fp8_quant_act_128x1_t(_ptr(x), M, N, ldx, _ptr(qt), _ld(qt), _ptr(st),
+                                         st.stride(0), _stream(x)), "fp8_quant_act_128x1_t")
     return qt, st
 
 
@@ -338,10 +352,11 @@ def fp8_block_gemm_rowscaled(a, sa, b, sb, out=None, out_dtype=torch.float32):
     _need_device(a, sa, b, sb, out)
     if out is None:
         out = torch.empty(M, N, dtype=out_dtype, device=a.device)
-    _check(lib.fp8_block_gemm_rowscaled(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
-                                        _ld(b), _ptr(sb), sb.stride(0), _ptr(out), _ld(out),
-                                        _out_kind(out.dtype), M, N, K, _stream(a)),
-           "fp8_block_gemm_rowscaled")
+    with torch.cuda.device(a.device):
+        _check(lib.fp8_block_gemm_rowscaled(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
+                                            _ld(b), _ptr(sb), sb.stride(0), _ptr(out), _ld(out),
+                                            _out_kind(out.dtype), M, N, K, _stream(a)),
+               "fp8_block_gemm_rowscaled")
     return out
 
 
@@ -369,10 +384,11 @@ def fp8_block_kgrouped_gemm_rowscaled(a, sa, b, sb, group_offsets, out=None,
     _need_device(a, sa, b, sb, group_offsets, out)
     if out is None:
         out = torch.empty(G, M, N, dtype=out_dtype, device=a.device)
-    _check(lib.fp8_block_kgrouped_gemm_rowscaled(
-        _ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b), _ld(b), _ptr(sb), sb.stride(0),
-        _ptr(out), out.stride(1), out.stride(0), _out_kind(out.dtype), _ptr(group_offsets), G, M,
-        N, T, _stream(a)), "fp8_block_kgrouped_gemm_rowscaled")
+    with torch.cuda.device(a.device):
+        _check(lib.fp8_block_kgrouped_gemm_rowscaled(
+            _ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b), _ld(b), _ptr(sb), sb.stride(0),
+            _ptr(out), out.stride(1), out.stride(0), _out_kind(out.dtype), _ptr(group_offsets),
+            G, M, N, T, _stream(a)), "fp8_block_kgrouped_gemm_rowscaled")
     return out
 
 
@@ -430,9 +446,10 @@ def fp8_block_gemm(a, sa, b, sb, out=None, out_dtype=torch.bfloat16, workspace=N
         out = torch.empty(M, N, dtype=out_dtype, device=a.device)
     workspace, ws_bytes = _workspace(a_kind, M, N, K, workspace, a.device)
     ldsa = sa.stride(0) if sa is not None else 0
-    _check(lib.fp8_block_gemm(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
-                              _ptr(sb), _ptr(out), _ld(out), _out_kind(out.dtype), M, N, K,
-                              _ptr(workspace), ws_bytes, _stream(a)), "fp8_block_gemm")
+    with torch.cuda.device(a.device):
+        _check(lib.fp8_block_gemm(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
+                                  _ptr(sb), _ptr(out), _ld(out), _out_kind(out.dtype), M, N, K,
+                                  _ptr(workspace), ws_bytes, _stream(a)), "fp8_block_gemm")
     return out
 
 
@@ -466,10 +483,11 @@ def fp8_block_grouped_gemm(a, sa, b, sb, group_offsets, out=None, out_dtype=torc
     _need_device(a, sa, b, sb, group_offsets, out)
     if out is None:
         out = torch.empty(M_total, N, dtype=out_dtype, device=a.device)
-    _check(lib.fp8_block_grouped_gemm(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
-                                      b.stride(1), b.stride(0), _ptr(sb), _ptr(out), _ld(out),
-                                      _out_kind(out.dtype), _ptr(group_offsets), G, M_total, N,
-                                      K, None, 0, _stream(a)), "fp8_block_grouped_gemm")
+    with torch.cuda.device(a.device):
+        _check(lib.fp8_block_grouped_gemm(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
+                                          b.stride(1), b.stride(0), _ptr(sb), _ptr(out), _ld(out),
+                                          _out_kind(out.dtype), _ptr(group_offsets), G, M_total, N,
+                                          K, None, 0, _stream(a)), "fp8_block_grouped_gemm")
     return out
 
 
@@ -501,10 +519,12 @@ def fp8_block_gemm_e4m3_out(a, sa, b, sb, qc=None, sc=None, workspace=None):
     qc, sc = _e4m3_outputs(M, N, qc, sc, a.device)
     workspace, ws_bytes = _workspace(a_kind, M, N, K, workspace, a.device)
     ldsa = sa.stride(0) if sa is not None else 0
-    _check(lib.fp8_block_gemm_e4m3_out(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
-                                       _ptr(sb), _ptr(qc), _ld(qc), _ptr(sc), sc.stride(0), M, N,
-                                       K, _ptr(workspace), ws_bytes, _stream(a)),
-           "fp8_block_gemm_e4m3_out")
+    with torch.cuda.device(a.device):
+        _check(lib.fp8_block_gemm_e4m3_out(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b),
+                                           _ld(b), _ptr(sb), _ptr(qc), _ld(qc), _ptr(sc),
+                                           sc.stride(0), M, N, K, _ptr(workspace), ws_bytes,
+                                           _stream(a)),
+               "fp8_block_gemm_e4m3_out")
     return qc, sc
 
 
@@ -518,10 +538,11 @@ def fp8_block_grouped_gemm_e4m3_out(a, sa, b, sb, group_offsets, qc=None, sc=Non
     _e4m3_check(M_total, N, qc, sc)
     _need_device(a, sa, b, sb, group_offsets, qc, sc)
     qc, sc = _e4m3_outputs(M_total, N, qc, sc, a.device)
-    _check(lib.fp8_block_grouped_gemm_e4m3_out(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
-                                               b.stride(1), b.stride(0), _ptr(sb), _ptr(qc),
-                                               _ld(qc), _ptr(sc), sc.stride(0),
-                                               _ptr(group_offsets), G, M_total, N, K, None, 0,
-                                               _stream(a)),
-           "fp8_block_grouped_gemm_e4m3_out")
+    with torch.cuda.device(a.device):
+        _check(lib.fp8_block_grouped_gemm_e4m3_out(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
+                                                   b.stride(1), b.stride(0), _ptr(sb), _ptr(qc),
+                                                   _ld(qc), _ptr(sc), sc.stride(0),
+                                                   _ptr(group_offsets), G, M_total, N, K, None, 0,
+                                                   _stream(a)),
+               "fp8_block_grouped_gemm_e4m3_out")
     return qc, sc
