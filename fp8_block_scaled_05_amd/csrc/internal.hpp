@@ -21,9 +21,9 @@ struct GemmArgs {
   int64_t ldc;
   float* sc;     // E4M3 output only: scale of row m, 128-column block nb at sc[nb*ldsc + m]
   int64_t ldsc;
-  int64_t M;  // rows (dense) or M_total (grouped)
+  int64_t M;  // rows (dense) or M_total (grouped rows)
   int64_t N;
-  int64_t K;
+  int64_t K;  // contraction length (grouped along K: all groups' K_total)
   const int32_t* group_offsets;  // grouped only, device, G+1 entries
   int64_t G;
   int64_t c_group_stride;        // grouped along K: elements between the groups' outputs

@@ -5,9 +5,13 @@
 // DeepSeek-V3's efficiency", sections "Fine-grained quantization strategy"
 // and "Dynamic scaling and online quantization").
 //
-// Both kernels are HBM-bound streams (2 bytes in, 1 byte + a scale out per
-// element).  Each 16-lane DPP row owns one 256-byte row segment of a group:
-// 16-byte loads, a DPP max across the row, the scale, then 8-byte code stores.
+// All kernels here are HBM-bound streams (2 bytes in, 1 byte + a scale out
+// per element).  Each 16-lane DPP row owns one 256-byte row segment of a
+// group: 16-byte loads, a DPP max across the row, the scale, then 8-byte code
+// stores.  Kernels: the 1x128 activation quantizer, the 128x128 weight
+// quantizer (optionally also writing W^T), both in one launch for a linear
+// layer's two operands, and the 128-token transposed activation quantizer of
+// the weight gradient.
 
 #include "device.hpp"
 #include "internal.hpp"
