@@ -179,3 +179,27 @@ def test_linear_pair_full_size_equals_single_calls(fp8bs):
     qr, sr = oracle.quant_w_128x128(wb)
     gu.assert_same_bits(gu.host(qw[-256:]), qr, "weight codes, last bands")
     gu.assert_same_bits(gu.host(sw[-2:]), sr, "weight scales, last bands")
+
+
+def test_linear_pair_strided_operands_and_outputs(fp8bs):
+    """Row strides above K for both inputs and both code outputs, and an
+    activation-scale leading dimension above M: every byte outside the
+    operands' extents is left as it was."""
+    M, N, K = 100, 300, 256
+    xb = synth.bf16_bits(synth.act(M, K + 128, case=420, tensor=0))
+    wb = synth.bf16_bits(synth.weight(N, K + 256, case=420, tensor=1))
+    x = gu.bf16_from_bits(xb)[:, 64:64 + K]          # ldx = K + 128
+    w = gu.bf16_from_bits(wb)[:, 128:128 + K]        # ldw = K + 256
+    q_full = torch.full((M, K + 64), 0x5A, dtype=torch.uint8, device="cuda")
+    s_full = torch.full((K // 128, M + 28), -1.0, dtype=torch.float32, device="cuda")
+    qw_full = torch.full((N, K + 32), 0xA5, dtype=torch.uint8, device="cuda")
+    q, s, qw, sw = fp8bs.fp8_quant_linear(x, w, q_full[:, :K], s_full[:, :M], qw_full[:, :K])
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_act_1x128(xb[:, 64:64 + K])
+    qwr, swr = oracle.quant_w_128x128(wb[:, 128:128 + K])
+    gu.assert_same_bits(gu.host(q_full[:, :K]), qr, "act codes")
+    gu.assert_same_bits(gu.host(s_full[:, :M]), sr, "act scales")
+    gu.assert_same_bits(gu.host(qw_full[:, :K]), qwr, "weight codes")
+    gu.assert_same_bits(gu.host(sw), swr, "weight scales")
+    assert torch.all(q_full[:, K:] == 0x5A) and torch.all(qw_full[:, K:] == 0xA5)
+    assert torch.all(s_full[:, M:] == -1.0)
