@@ -43,6 +43,8 @@ def _run(fp8bs, qa, sa, qw, sw, offsets, out_dtype):
     ([513, 0, 256, 257, 1], 640, 384, torch.bfloat16),
     # last tile-rows of exactly 128 rows (half-height), 129 (full height), 44
     ([384, 129, 300], 256, 256, torch.float32),
+    # one K group (the pipeline's prologue and drain only), N of one block
+    ([100, 0, 3, 260], 128, 128, torch.float32),
 ])
 def test_grouped_all_outputs(fp8bs, sizes, N, K, out):
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
