@@ -55,3 +55,30 @@ def test_full_size_skinny_sampled(fp8bs, M):
         gu.assert_same_bits(gu.host(qw_g[nb * 128:(nb + 1) * 128]), qw, f"band {nb} codes")
         C, B = oracle.block_gemm(qa, sa, qw, sw)
         gu.check_gemm(ch[:, nb * 128:(nb + 1) * 128], C, B, bf16=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 384), (16, 300, 1024), (33, 128, 256),
+                                   (64, 640, 512)])
+def test_in_call_quantization_equals_two_step(fp8bs, M, N, K):
+    """A bf16 A quantized inside the call gives bitwise the output of
+    quantizing it first and multiplying the codes (same codes, scales, MFMA
+    and promotion arithmetic); bf16 and E4M3 outputs, a strided A (lda > K),
+    a ragged N."""
+    full = synth.act(M, K + 128, case=660 + M, tensor=0, device="cuda")
+    x = full[:, 64:64 + K]
+    w = synth.weight(N, K, case=660 + M, tensor=1, device="cuda")
+    qw, sw = fp8bs.fp8_quant_w_128x128(w)
+    sa_f = torch.full((K // 128, M), -1.0, dtype=torch.float32, device="cuda")
+    c_f = fp8bs.fp8_block_gemm(x, sa_f, qw, sw, out_dtype=torch.bfloat16)
+    qa, sa = fp8bs.fp8_quant_act_1x128(x)
+    c_2 = fp8bs.fp8_block_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    gu.assert_same_bits(gu.host(sa_f), gu.host(sa), "in-kernel scales")
+    gu.assert_same_bits(gu.host(c_f.view(torch.int16)), gu.host(c_2.view(torch.int16)),
+                        "bf16 output")
+    if N % 128 == 0:
+        q_f, s_f = fp8bs.fp8_block_gemm_e4m3_out(x, None, qw, sw)
+        q_2, s_2 = fp8bs.fp8_block_gemm_e4m3_out(qa, sa, qw, sw)
+        torch.cuda.synchronize()
+        gu.assert_same_bits(gu.host(q_f), gu.host(q_2), "E4M3 output codes")
+        gu.assert_same_bits(gu.host(s_f), gu.host(s_2), "E4M3 output scales")
