@@ -15,7 +15,9 @@
 // (BM/WM) x (BN/WN) sub-tile made of 16x16 MFMA tiles.  Every K group of A
 // and B is copied HBM->LDS by direct buffer_load ... lds (no register
 // staging) into one of STAGES LDS buffers; the group's scales go through
-// registers into a separate LDS array.  STAGES-1 groups are in flight while
+// registers into a separate LDS array (with block-scaled B as the finished
+// promotion factors S_A(row) * S_W(block), so that the MFMA loop does no
+// arithmetic for them).  STAGES-1 groups are in flight while
 // one feeds the MFMAs, and the copies of the next group are spread between
 // the MFMA rows.  LDS rows are 128 bytes; the eight 16-byte chunks of a row
 // are stored XOR-swizzled (lds_swizzle) so that the fragment reads are free
@@ -59,6 +61,9 @@ struct Cfg {
   static constexpr int SB_COUNT = (BN + 127) / 128;
   // B scales per 128x128 block (false) or per row and K group (RowScaledB)
   static constexpr bool ROWB = false;
+  // block-scaled B: the staged scales are the promotion factors
+  // S_A(row) * S_W(block) for each of the tile's SB_COUNT weight blocks
+  static constexpr bool PREMUL = true;
   // LDS stage: A rows | B rows; the scales of a stage live in a separate
   // array (activation scales, then weight-block scales) so that the compiler
   // can tell their register->LDS writes from the in-flight tile copies
@@ -67,16 +72,17 @@ struct Cfg {
   static constexpr int STAGE_BYTES = B_OFF + BN * 128;
   // 1 KB (8 rows) per wave-wide direct load
   static constexpr int TILE_LOADS = (BM + BN) / 8 / NWAVES;
-  // the scales go through registers (one fp32 per thread per item: the BM
-  // activation scales, then the SB_COUNT weight-block scales of the tile, or
-  // with row-scaled B its BN row scales) and are written to LDS after the
-  // compute; SREG loads per thread per stage (room for BN B scales in both
-  // cases: the block case repeats its last scale in the spare slots)
-  static constexpr int SCALE_ITEMS = BM + BN;
+  // the scales go through registers and are written to LDS after the
+  // compute, SREG items per thread per stage.  Block-scaled B: item
+  // nb * BM + row is the factor S_A(row) * S_W(nb) of tile row `row` and the
+  // tile's weight block nb, loaded as its two scales and multiplied before
+  // the LDS write (spare items repeat the last block's factors)
+  static constexpr int SCALE_ITEMS = SB_COUNT * BM;
   static constexpr int SREG = (SCALE_ITEMS + THREADS - 1) / THREADS;
   // every thread writes its SREG slots (no branch, so no merged wait counts)
   static constexpr int SCALE_FLOATS = SREG * THREADS;
-  static constexpr int LOADS = TILE_LOADS + SREG;  // vector-memory ops per wave per stage
+  // vector-memory ops per wave per stage (two scale loads per item)
+  static constexpr int LOADS = TILE_LOADS + 2 * SREG;
   static_assert((BM + BN) / 8 % NWAVES == 0, "tile loads must split evenly over waves");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave sub-tile must be whole MFMA tiles");
   static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns must share one weight block");
@@ -91,7 +97,14 @@ struct Cfg {
 // are both token-grouped activations.
 template <class C>
 struct RowScaledB : C {
-  static constexpr bool ROWB = true;
+  // items: the BM activation scales, then the BN row scales of B (the
+  // factors differ per output element, so they are formed in the MFMA loop)
+  static constexpr bool ROWB = true, PREMUL = false;
+  static constexpr int SCALE_ITEMS = C::BM + C::BN;
+  static constexpr int SREG = (SCALE_ITEMS + C::THREADS - 1) / C::THREADS;
+  static constexpr int SCALE_FLOATS = SREG * C::THREADS;
+  static constexpr int LOADS = C::TILE_LOADS + SREG;
+  static_assert(LOADS <= 63, "vmcnt range");
 };
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
@@ -270,6 +283,15 @@ template <class C>
 struct LoadPlan {
   uint32_t tile[C::TILE_LOADS];
   int32_t scale[C::SREG];  // element offset from the tile's S_A (or S_W) column base
+  int32_t scaleb[C::SREG]; // factor items: element offset of the S_W block scale
+};
+
+// One stage's scales in registers: the S_A (or row-scaled S_W) value of each
+// item, and with block-scaled B the item's S_W block scale.
+template <class C>
+struct ScaleRegs {
+  float a[C::SREG];
+  float b[C::PREMUL ? C::SREG : 1];
 };
 
 template <class C>
@@ -301,18 +323,21 @@ __device__ __forceinline__ void make_plan(const GemmArgs& p, const TileCoords& t
 #pragma unroll
   for (int s = 0; s < C::SREG; ++s) {
     const int item = (int)threadIdx.x + s * C::THREADS;
-    if (item < C::BM) {
+    if constexpr (C::PREMUL) {
+      // item = nb * BM + row: factor of tile row `row` and weight block nb
+      // (blocks past the end of N, and spare items, repeat the last)
+      const int row = item % C::BM;
+      const int64_t nbl = NB - 1 - t.col0 / 128;
+      int nb = item / C::BM;
+      nb = nb < C::SB_COUNT ? nb : C::SB_COUNT - 1;
+      lp.scale[s] = row < rows_a ? row : rows_a - 1;
+      lp.scaleb[s] = (int)((nb < nbl ? nb : nbl) * p.sb_ld);
+    } else if (item < C::BM) {
       lp.scale[s] = item < rows_a ? item : rows_a - 1;
-    } else if constexpr (C::ROWB) {
-      // row scale of tile column j (columns past N repeat the last)
+    } else {
+      // row-scaled B: row scale of tile column j (columns past N repeat the last)
       const int j = item - C::BM;
       lp.scale[s] = j < rows_b ? j : rows_b - 1;
-    } else {
-      // weight-block scale j of the tile (items past the end repeat the last)
-      const int64_t nbl = NB - 1 - t.col0 / 128;  // last block index within the tile
-      int j = item - C::BM;
-      j = j < C::SB_COUNT ? j : C::SB_COUNT - 1;
-      lp.scale[s] = (int)((j < nbl ? j : nbl) * p.sb_ld);
     }
   }
 }
@@ -358,7 +383,7 @@ __device__ __forceinline__ void issue_copy(const GemmArgs& p, const Rsrc& rs,
 template <class C>
 __device__ __forceinline__ void load_scales(const GemmArgs& p, const TileCoords& t,
                                             const LoadPlan<C>& lp, int64_t kb,
-                                            float (&v)[C::SREG]) {
+                                            ScaleRegs<C>& v) {
   const float* sa = p.sa + (t.kb0 + kb) * p.ldsa + t.row0;
   const float* sb = C::ROWB ? t.sb + (t.kb0 + kb) * p.sb_ld + t.col0
                             : t.sb + (t.col0 / 128) * p.sb_ld + t.kb0 + kb;
@@ -366,15 +391,22 @@ __device__ __forceinline__ void load_scales(const GemmArgs& p, const TileCoords&
   for (int s = 0; s < C::SREG; ++s) {
     const int item = (int)threadIdx.x + s * C::THREADS;
     // one load instruction per item slot on every wave (uniform vmcnt counts)
-    const float* src = item < C::BM ? sa : sb;
-    v[s] = src[lp.scale[s]];
+    if constexpr (C::PREMUL) {
+      (void)item;
+      v.a[s] = sa[lp.scale[s]];
+      v.b[s] = sb[lp.scaleb[s]];
+    } else {
+      const float* src = item < C::BM ? sa : sb;
+      v.a[s] = src[lp.scale[s]];
+    }
   }
 }
 
 template <class C>
-__device__ __forceinline__ void store_scales(float* sc, const float (&v)[C::SREG]) {
+__device__ __forceinline__ void store_scales(float* sc, const ScaleRegs<C>& v) {
 #pragma unroll
-  for (int s = 0; s < C::SREG; ++s) sc[(int)threadIdx.x + s * C::THREADS] = v[s];
+  for (int s = 0; s < C::SREG; ++s)
+    sc[(int)threadIdx.x + s * C::THREADS] = C::PREMUL ? v.a[s] * v.b[s] : v.a[s];
 }
 
 template <class C>
@@ -411,7 +443,7 @@ __device__ __forceinline__ FragOffs frag_offsets(int wm, int wn, int lane) {
   f.a_hi = C::A_OFF + (wm * C::TM + l16) * 128 + (slot0 ^ 1) * 16;
   f.b_lo = C::B_OFF + (wn * C::TN + l16) * 128 + slot0 * 16;
   f.b_hi = C::B_OFF + (wn * C::TN + l16) * 128 + (slot0 ^ 1) * 16;
-  f.sa = wm * C::TM + 4 * (lane >> 4);
+  f.sa = wm * C::TM + 4 * (lane >> 4) + (C::PREMUL ? (wn * C::TN) / 128 * C::BM : 0);
   // Lanes 16g..16g+15 need the activation scales of rows 16 i + 4 g + r
   // (i < FM, r < 4) of the wave's sub-tile: value v = 4 i + r.  With FM a
   // multiple of 4, lane 16g + k loads values v = PV k .. PV k + PV - 1
@@ -456,10 +488,11 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   // they have a whole step of slack and are spread over all rows.
   constexpr int ISSUE_ROWS = C::STAGES == 2 ? (C::FM + 1) / 2 : C::FM;
   constexpr int PER_ROW = (C::TILE_LOADS + ISSUE_ROWS - 1) / ISSUE_ROWS;
-  // block-scaled B: one weight-block scale for the wave's columns, folded
-  // into the row factors; row-scaled B: the lane's FN column scales, applied
-  // per MFMA tile
-  const float sbv = C::ROWB ? 1.0f : sc[C::BM + (wn * C::TN) / 128];
+  // block-scaled B: the stage holds the row factors of the wave's weight
+  // block (fo.sa points into them); row-scaled B: the lane's FN column
+  // scales, applied per MFMA tile
+  static_assert(C::PREMUL != C::ROWB, "block-scaled B stages finished factors");
+  (void)wn;
   float sbj[C::FN];
   if constexpr (C::ROWB) {
     if constexpr (C::FN % 4 == 0) {
@@ -477,10 +510,10 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
     }
   }
   const float* w4 = sc + fo.sa;
-  // FM % 4 == 0: each lane holds PV of its row's activation scales (one LDS
-  // read per group instead of one 16-byte read per MFMA row) and the
-  // promotion factors take them by DPP row broadcast
-  constexpr bool DPPS = C::FM % 4 == 0;
+  // row-scaled B with FM % 4 == 0: each lane holds PV of its row's
+  // activation scales (one LDS read per group instead of one 16-byte read
+  // per MFMA row) and the rows' lanes take them by DPP row broadcast
+  constexpr bool DPPS = C::FM % 4 == 0 && C::ROWB;
   constexpr int PV = DPPS ? C::FM / 4 : 1;
   float sv[PV];
   if constexpr (DPPS) {
@@ -515,19 +548,20 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
     if (t < NM) {
       const int i = t / C::FN, j = t % C::FN;
       if (j == 0) {
-        // this row's promotion factors S_A(row) * S_W; prefetch the next row
+        // this row's factors (S_A(row) * S_W, or S_A(row) with row-scaled B);
+        // prefetch the next row
         if constexpr (DPPS) {
           // row 16 i + 4 g + r: value v = 4 i + r, held by lane v / PV (slot v % PV)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int v = 4 * i + r;
-            w[i % WS][r] = row_bcast_k(v / PV, sv[v % PV]) * sbv;
+            w[i % WS][r] = row_bcast_k(v / PV, sv[v % PV]);
           }
         } else {
-          w[i % WS][0] = s4[i & 1].x * sbv;
-          w[i % WS][1] = s4[i & 1].y * sbv;
-          w[i % WS][2] = s4[i & 1].z * sbv;
-          w[i % WS][3] = s4[i & 1].w * sbv;
+          w[i % WS][0] = s4[i & 1].x;
+          w[i % WS][1] = s4[i & 1].y;
+          w[i % WS][2] = s4[i & 1].z;
+          w[i % WS][3] = s4[i & 1].w;
         }
         if (i + 1 < C::FM) {
           af[(i + 1) & 1] = load_frag(st, fo.a_lo, fo.a_hi, 16 * (i + 1) * 128);
@@ -737,34 +771,30 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
   // real group, so the drain's waits (which count real groups only) still
   // cover them.
   constexpr int SLEAD = C::STAGES - 2;
-  float carry[SLEAD > 0 ? SLEAD : 1][C::SREG];
+  ScaleRegs<C> carry[SLEAD > 0 ? SLEAD : 1];
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s) {
     const int64_t g = s < KB ? s : KB - 1;
-    float sv[C::SREG];
+    ScaleRegs<C> sv;
     load_scales<C>(p, t, lp, g, sv);
     issue_stage<C>(p, rs, lp, g, stg(s), wave);
     if (s == 0) {
       store_scales<C>(scl(0), sv);
     } else {
-#pragma unroll
-      for (int r = 0; r < C::SREG; ++r) carry[s - 1][r] = sv[r];
+      carry[s - 1] = sv;
     }
   }
   // end of the step of group k (stage index u = k % STAGES): write the scales
   // of group k + 1, then shift the ring (cur: the scales loaded this step,
   // group k + STAGES - 1)
-  auto retire_scales = [&](int u, const float (&cur)[C::SREG], bool store_next) {
+  auto retire_scales = [&](int u, const ScaleRegs<C>& cur, bool store_next) {
     if constexpr (SLEAD == 0) {
       if (store_next) store_scales<C>(scl((u + 1) % C::STAGES), cur);
     } else {
       if (store_next) store_scales<C>(scl((u + 1) % C::STAGES), carry[0]);
 #pragma unroll
-      for (int d = 0; d + 1 < SLEAD; ++d)
-#pragma unroll
-        for (int r = 0; r < C::SREG; ++r) carry[d][r] = carry[d + 1][r];
-#pragma unroll
-      for (int r = 0; r < C::SREG; ++r) carry[SLEAD - 1][r] = cur[r];
+      for (int d = 0; d + 1 < SLEAD; ++d) carry[d] = carry[d + 1];
+      carry[SLEAD - 1] = cur;
     }
   };
 
@@ -788,7 +818,7 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
       wait_and_sync(C::STAGES - 2);
       uint8_t* const nxt = stg((u + C::STAGES - 1) % C::STAGES);
       const int64_t kn = kb + u + C::STAGES - 1;
-      float sv[C::SREG];
+      ScaleRegs<C> sv;
       load_scales<C>(p, t, lp, kn, sv);
       // keep the scale loads ahead of this step's tile copies (in-order
       // completion then lets their wait leave the tile copies in flight)
@@ -809,9 +839,7 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
       wait_and_sync((int)(last - k));
       uint8_t* const nxt = stg((u + C::STAGES - 1) % C::STAGES);
       const bool refill = k + C::STAGES - 1 < KB;
-      float sv[C::SREG];
-#pragma unroll
-      for (int r = 0; r < C::SREG; ++r) sv[r] = 0.f;
+      ScaleRegs<C> sv{};
       if (refill) {
         load_scales<C>(p, t, lp, k + C::STAGES - 1, sv);
         issue_stage<C>(p, rs, lp, k + C::STAGES - 1, nxt, wave);
