@@ -43,38 +43,6 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Lane K of each row of 16 lanes, broadcast to the whole row (row_newbcast).
-template <int K>
-__device__ __forceinline__ float row_bcast(float v) {
-  static_assert(K >= 0 && K < 16, "lane within a DPP row");
-  // every lane has a source lane, so bound_ctrl never applies; setting it
-  // lets the compiler fold the move into the instruction that uses it
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xF, 0xF, true));
-}
-
-// row_bcast with the lane as a value; k must fold to a constant after
-// unrolling (each case is a single DPP move).
-__device__ __forceinline__ float row_bcast_k(int k, float v) {
-  switch (k) {
-    case 0: return row_bcast<0>(v);
-    case 1: return row_bcast<1>(v);
-    case 2: return row_bcast<2>(v);
-    case 3: return row_bcast<3>(v);
-    case 4: return row_bcast<4>(v);
-    case 5: return row_bcast<5>(v);
-    case 6: return row_bcast<6>(v);
-    case 7: return row_bcast<7>(v);
-    case 8: return row_bcast<8>(v);
-    case 9: return row_bcast<9>(v);
-    case 10: return row_bcast<10>(v);
-    case 11: return row_bcast<11>(v);
-    case 12: return row_bcast<12>(v);
-    case 13: return row_bcast<13>(v);
-    case 14: return row_bcast<14>(v);
-    default: return row_bcast<15>(v);
-  }
-}
-
 // Maximum over the 16 lanes of a DPP row; every lane receives it.  The steps
 // swap neighbours (quad_perm 1,0,3,2), pairs (quad_perm 2,3,0,1), quads
 // (row_half_mirror) and halves (row_mirror).  Max is exact and

@@ -428,7 +428,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 struct FragOffs {
   int a_lo, a_hi, b_lo, b_hi;  // K chunks 2g and 2g+1 of lane group g
   int sa;                      // float index of the lane's first activation scale
-  int sv;                      // float index of the scales this lane loads for its row of 16
   int sbc;                     // row-scaled B: float index of the lane's first column scale
 };
 
@@ -444,21 +443,9 @@ __device__ __forceinline__ FragOffs frag_offsets(int wm, int wn, int lane) {
   f.b_lo = C::B_OFF + (wn * C::TN + l16) * 128 + slot0 * 16;
   f.b_hi = C::B_OFF + (wn * C::TN + l16) * 128 + (slot0 ^ 1) * 16;
   f.sa = wm * C::TM + 4 * (lane >> 4) + (C::PREMUL ? (wn * C::TN) / 128 * C::BM : 0);
-  // Lanes 16g..16g+15 need the activation scales of rows 16 i + 4 g + r
-  // (i < FM, r < 4) of the wave's sub-tile: value v = 4 i + r.  With FM a
-  // multiple of 4, lane 16g + k loads values v = PV k .. PV k + PV - 1
-  // (PV = FM / 4 consecutive rows), which the rows' lanes fetch by DPP.
-  if constexpr (C::FM % 4 == 0) {
-    constexpr int PV = C::FM / 4;
-    const int v0 = PV * l16;
-    f.sv = f.sa + 16 * (v0 / 4) + v0 % 4;
-  } else {
-    f.sv = f.sa;
-  }
   // the lane's FN output columns are consecutive (permuted B staging)
   f.sbc = C::BM + wn * C::TN + C::FN * l16;
-  asm volatile("" : "+v"(f.a_lo), "+v"(f.a_hi), "+v"(f.b_lo), "+v"(f.b_hi), "+v"(f.sa),
-               "+v"(f.sv));
+  asm volatile("" : "+v"(f.a_lo), "+v"(f.a_hi), "+v"(f.b_lo), "+v"(f.b_hi), "+v"(f.sa));
   return f;
 }
 
@@ -509,23 +496,8 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
       for (int q = 0; q < C::FN; ++q) sbj[q] = sc[fo.sbc + q];
     }
   }
+  // a lane's 4 rows of MFMA row i: one 16-byte LDS read (rows 16 i + 4 g .. + 3)
   const float* w4 = sc + fo.sa;
-  // row-scaled B with FM % 4 == 0: each lane holds PV of its row's
-  // activation scales (one LDS read per group instead of one 16-byte read
-  // per MFMA row) and the rows' lanes take them by DPP row broadcast
-  constexpr bool DPPS = C::FM % 4 == 0 && C::ROWB;
-  constexpr int PV = DPPS ? C::FM / 4 : 1;
-  float sv[PV];
-  if constexpr (DPPS) {
-    if constexpr (PV == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(sc + fo.sv);
-      sv[0] = v.x;
-      sv[1] = v.y;
-    } else {
-#pragma unroll
-      for (int q = 0; q < PV; ++q) sv[q] = sc[fo.sv + q];
-    }
-  }
   v8i bf[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) bf[j] = load_frag(st, fo.b_lo, fo.b_hi, 16 * j * 128);
@@ -533,7 +505,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   float4 s4[2];
   float w[WS][4];
   af[0] = load_frag(st, fo.a_lo, fo.a_hi, 0);
-  if constexpr (!DPPS) s4[0] = *reinterpret_cast<const float4*>(w4);
+  s4[0] = *reinterpret_cast<const float4*>(w4);
   v4f ring[RING];
 #pragma unroll
   for (int t = 0; t < NM + RING; ++t) {
@@ -550,23 +522,13 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
       if (j == 0) {
         // this row's factors (S_A(row) * S_W, or S_A(row) with row-scaled B);
         // prefetch the next row
-        if constexpr (DPPS) {
-          // row 16 i + 4 g + r: value v = 4 i + r, held by lane v / PV (slot v % PV)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = 4 * i + r;
-            w[i % WS][r] = row_bcast_k(v / PV, sv[v % PV]);
-          }
-        } else {
-          w[i % WS][0] = s4[i & 1].x;
-          w[i % WS][1] = s4[i & 1].y;
-          w[i % WS][2] = s4[i & 1].z;
-          w[i % WS][3] = s4[i & 1].w;
-        }
+        w[i % WS][0] = s4[i & 1].x;
+        w[i % WS][1] = s4[i & 1].y;
+        w[i % WS][2] = s4[i & 1].z;
+        w[i % WS][3] = s4[i & 1].w;
         if (i + 1 < C::FM) {
           af[(i + 1) & 1] = load_frag(st, fo.a_lo, fo.a_hi, 16 * (i + 1) * 128);
-          if constexpr (!DPPS)
-            s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(w4 + 16 * (i + 1));
+          s4[(i + 1) & 1] = *reinterpret_cast<const float4*>(w4 + 16 * (i + 1));
         }
       }
       ring[t % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
