@@ -427,7 +427,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // flight to the other stages (an untagged read waits for every copy).
 struct FragOffs {
   int a_lo, a_hi, b_lo, b_hi;  // K chunks 2g and 2g+1 of lane group g
-  int sa;                      // float index of the lane's first activation scale
+  int sa;                      // float index of the lane's first row factor (block-scaled B:
+                               // in its wave's weight block) or activation scale (row-scaled B)
   int sbc;                     // row-scaled B: float index of the lane's first column scale
 };
 
@@ -464,7 +465,7 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* st, int lo, int hi, int 
 template <class C, bool REFILL, class Refill>
 __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc,
                                               const FragOffs& fo, v4f (&acc)[C::FM][C::FN],
-                                              int wn, Refill&& issue_copy_n) {
+                                              Refill&& issue_copy_n) {
   constexpr int NM = C::FM * C::FN;
   constexpr int RING = 4;
   // the promotion factors of row i are read until step i*FN + FN - 1 + RING
@@ -479,7 +480,6 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, const float* sc
   // block (fo.sa points into them); row-scaled B: the lane's FN column
   // scales, applied per MFMA tile
   static_assert(C::PREMUL != C::ROWB, "block-scaled B stages finished factors");
-  (void)wn;
   float sbj[C::FN];
   if constexpr (C::ROWB) {
     if constexpr (C::FN % 4 == 0) {
@@ -785,7 +785,7 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
       // keep the scale loads ahead of this step's tile copies (in-order
       // completion then lets their wait leave the tile copies in flight)
       __builtin_amdgcn_sched_barrier(0);
-      compute_stage<C, true>(stg(u), scl(u), fo, acc, wn, [&](int c) {
+      compute_stage<C, true>(stg(u), scl(u), fo, acc, [&](int c) {
         issue_copy<C>(p, rs, lp, kn, nxt, wave, c);
       });
       retire_scales(u, sv, true);
@@ -806,7 +806,7 @@ __device__ __forceinline__ void block_gemm_body(const GemmArgs& p, const TileCoo
         load_scales<C>(p, t, lp, k + C::STAGES - 1, sv);
         issue_stage<C>(p, rs, lp, k + C::STAGES - 1, nxt, wave);
       }
-      compute_stage<C, false>(stg(u % C::STAGES), scl(u % C::STAGES), fo, acc, wn, [](int) {});
+      compute_stage<C, false>(stg(u % C::STAGES), scl(u % C::STAGES), fo, acc, [](int) {});
       retire_scales(u % C::STAGES, sv, SLEAD == 0 ? refill : k + 1 < KB);
     }
   }
