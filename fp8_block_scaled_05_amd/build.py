@@ -1,4 +1,5 @@
-"""Build libfp8bs.so (hand-written HIP for gfx950) in-tree with hipcc.
+"""Build libfp8bs.so (hand-written HIP for gfx950) in-tree with hipcc, and
+the test-only kernel libraries under tests/native.
 
 Usage: ``python -m fp8_block_scaled_05_amd.build`` (also called by
 ``__graft_entry__.build()``).  Always recompiles.
@@ -17,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8bs.so")
+# test-only kernels (never part of libfp8bs): tests/native/*.hip, each built
+# into its own library next to its source, with the package's device headers
+TEST_NATIVE = os.path.join(ROOT, "tests", "native")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are disabled for all device code; the
@@ -60,6 +64,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    for src in sorted(glob.glob(os.path.join(TEST_NATIVE, "*.hip"))):
+        out = os.path.join(TEST_NATIVE, "lib" + os.path.basename(src)[:-4] + ".so")
+        cmd = [hipcc, *DEVICE_FLAGS, "-I", CSRC, "-shared", src, "-o", out + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        os.replace(out + ".tmp", out)
     return LIB
 
 

@@ -34,6 +34,8 @@
 // or grouped (MoE) tile schedules.
 #pragma once
 
+#include <atomic>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -844,7 +846,7 @@ __device__ __forceinline__ void store_zero_tile(const GemmArgs& p, const TileCoo
 template <class C, class TAIL, int SCHED, int OUT>
 __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int64_t full) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(TAIL::THREADS == C::THREADS && TAIL::BN == C::BN && 2 * TAIL::BM == C::BM ||
+  static_assert((TAIL::THREADS == C::THREADS && TAIL::BN == C::BN && 2 * TAIL::BM == C::BM) ||
                     std::is_same<C, TAIL>::value, "tail tiles are half-height tiles");
   static_assert(SCHED != kGroupK || OUT != kOutE4M3, "grouped-K output is fp32 or bf16");
   constexpr int SB = C::STAGE_BYTES > TAIL::STAGE_BYTES ? C::STAGE_BYTES : TAIL::STAGE_BYTES;
@@ -921,17 +923,20 @@ __global__ __launch_bounds__(C::THREADS) void block_gemm_kernel(GemmArgs p, int6
 #endif
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device.  Any thread may
+// fill an entry; racing fills store the same value, and the relaxed atomics
+// make the race well defined.
 inline int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      cached[dev] = n;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <class C, int SCHED, class TAIL = C>
@@ -960,25 +965,21 @@ hipError_t launch(const GemmArgs& args, OutKind out, hipStream_t stream) {
   const dim3 grid((unsigned)blocks), block(C::THREADS);
   switch (out) {
     case kOutF32:
-      hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, SCHED, kOutF32>), grid, block, 0, stream,
-                         args, full);
-      break;
+      return launch_kernel(block_gemm_kernel<C, TAIL, SCHED, kOutF32>, grid, block, stream, args,
+                           full);
     case kOutBF16:
-      hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, SCHED, kOutBF16>), grid, block, 0, stream,
-                         args, full);
-      break;
+      return launch_kernel(block_gemm_kernel<C, TAIL, SCHED, kOutBF16>, grid, block, stream,
+                           args, full);
     default:
       if constexpr (C::BN % 128 == 0 && !C::ROWB && SCHED != kGroupK) {
-        hipLaunchKernelGGL((block_gemm_kernel<C, TAIL, SCHED, kOutE4M3>), grid, block, 0,
-                           stream, args, full);
+        return launch_kernel(block_gemm_kernel<C, TAIL, SCHED, kOutE4M3>, grid, block, stream,
+                             args, full);
       } else {
         // E4M3 output needs whole 128-column tiles; row-scaled B (weight
         // gradients) has fp32 and bf16 outputs only
         return hipErrorInvalidConfiguration;
       }
-      break;
   }
-  return hipGetLastError();
 }
 
 }  // namespace gemm

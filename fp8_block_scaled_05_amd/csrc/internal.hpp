@@ -4,7 +4,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace fp8bs {
+
+// Launch kernel `k` and return the status of this launch alone.  (Reading
+// hipGetLastError after a triple-chevron launch would also return, and
+// clear, an error that an earlier unrelated call left pending, and report it
+// as this call's failure.)  The arguments are converted to the kernel's
+// parameter types first, so the argument array matches its signature.
+template <class... P, class... A>
+hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                         A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count of the kernel");
+  std::tuple<P...> vals(std::forward<A>(args)...);
+  return std::apply(
+      [&](auto&... v) {
+        void* ptrs[] = {static_cast<void*>(&v)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, 0, stream);
+      },
+      vals);
+}
 
 struct GemmArgs {
   const uint8_t* a;

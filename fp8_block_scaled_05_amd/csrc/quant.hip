@@ -294,9 +294,8 @@ hipError_t launch_quant_act_128x1_t(const uint16_t* x, int64_t M, int64_t N, int
   const int64_t NB = N / 128;
   const int64_t blocks = (M / 128) * NB;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(quant_act_128x1_t_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x,
-                     NB, ldx, qt, ldqt, st, ldst);
-  return hipGetLastError();
+  return launch_kernel(quant_act_128x1_t_kernel, dim3((unsigned)blocks), dim3(256), stream, x,
+                       NB, ldx, qt, ldqt, st, ldst);
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -306,9 +305,8 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   const int64_t MB = (M + kActRowsPerWG - 1) / kActRowsPerWG;
   const int64_t blocks = MB * KB;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     ActArgs{x, M, KB, ldx, q, ldq, s, lds});
-  return hipGetLastError();
+  return launch_kernel(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(256), stream,
+                       ActArgs{x, M, KB, ldx, q, ldq, s, lds});
 }
 
 hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
@@ -319,14 +317,10 @@ hipError_t launch_quant_w(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
   const int64_t blocks = NB * KB;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const WArgs a{w, N, KB, ldw, q, ldq, s, qt, ldqt, st};
-  if (qt) {
-    hipLaunchKernelGGL(quant_w_128x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
-  } else {
-    hipLaunchKernelGGL(quant_w_128x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
-  }
-  return hipGetLastError();
+  if (qt) return launch_kernel(quant_w_128x128_kernel<true>, dim3((unsigned)blocks), dim3(256),
+                               stream, a);
+  return launch_kernel(quant_w_128x128_kernel<false>, dim3((unsigned)blocks), dim3(256), stream,
+                       a);
 }
 
 hipError_t launch_quant_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -339,10 +333,9 @@ hipError_t launch_quant_linear(const uint16_t* x, int64_t M, int64_t K, int64_t 
   const int64_t blocks = w_blocks + a_blocks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(quant_linear_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     ActArgs{x, M, KB, ldx, q, ldq, s, lds},
-                     WArgs{w, N, KB, ldw, qw, ldqw, sw, nullptr, 0, nullptr}, w_blocks);
-  return hipGetLastError();
+  return launch_kernel(quant_linear_kernel, dim3((unsigned)blocks), dim3(256), stream,
+                       ActArgs{x, M, KB, ldx, q, ldq, s, lds},
+                       WArgs{w, N, KB, ldw, qw, ldqw, sw, nullptr, 0, nullptr}, w_blocks);
 }
 
 }  // namespace fp8bs

@@ -169,14 +169,11 @@ hipError_t launch_quant_act_delayed(const uint16_t* x, int64_t M, int64_t K, int
   DelayArgs a{x, M, K / 128, ldx, q, ldq, s, lds, hist, ldh, H, step, stats};
   const int64_t blocks = (M + kRows - 1) / kRows * a.KB;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (per_tensor) {
-    hipLaunchKernelGGL(quant_act_delayed_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
-  } else {
-    hipLaunchKernelGGL(quant_act_delayed_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
-  }
-  return hipGetLastError();
+  if (per_tensor)
+    return launch_kernel(quant_act_delayed_kernel<true>, dim3((unsigned)blocks), dim3(256),
+                         stream, a);
+  return launch_kernel(quant_act_delayed_kernel<false>, dim3((unsigned)blocks), dim3(256), stream,
+                       a);
 }
 
 }  // namespace fp8bs

@@ -20,11 +20,19 @@
  *   GEMM:  C[m][n] = sum_kb S_A(m,kb) * S_W(n/128,kb) * P(m,n,kb), where
  *   P is the FP8 x FP8 dot product over the 128 K values of group kb,
  *   accumulated in FP32; the promotion is an FP32 multiply-add.
+ *   Inputs are finite.  A NaN or infinite input element is outside the
+ *   contract: the codes and scale of the group that holds it are unspecified
+ *   (no fault, and every other group is quantized as usual).
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE memory owned by the caller.  The library
- *     never allocates or frees device memory and keeps no state besides a
- *     thread-local record of the last HIP error.
+ *     never allocates or frees device memory.  Its state is a thread-local
+ *     record of the last HIP error and a per-device cache of the compute-unit
+ *     count (filled on first use by whichever thread calls; safe under
+ *     concurrent calls).
+ *   - FP8BS_ERR_HIP reports the failure of a launch made by this call only:
+ *     an error that an earlier, unrelated HIP call left pending is neither
+ *     returned nor cleared.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL means the default stream).  The return value is a
  *     synchronous status: FP8BS_OK means "validated and enqueued"; a device

@@ -1,0 +1,51 @@
+// Test-only kernel (not part of libfp8bs, not declared in fp8bs.h): runs a
+// contiguous range of float32 bit patterns through the library's own device
+// convert (cvt2_e4m3 in device.hpp: clamp to +-448, then the gfx950
+// round-to-nearest-even convert to OCP E4M3) and writes one code per input.
+// The GPU parity test compares the codes of every non-NaN float32 value with
+// the oracle's table-search encoder.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace {
+
+// codes[i] = E4M3(bits first + i) for i < n; 8 inputs per thread.
+__global__ __launch_bounds__(256) void convert_range_kernel(uint32_t first, int64_t n,
+                                                            uint8_t* __restrict__ codes) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i0 >= n) return;
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    x[j] = i0 + j < n ? __uint_as_float(first + (uint32_t)(i0 + j)) : 0.0f;
+  uint32_t lo = fp8bs::cvt2_e4m3<false>(x[0], x[1], 0u);
+  lo = fp8bs::cvt2_e4m3<true>(x[2], x[3], lo);
+  uint32_t hi = fp8bs::cvt2_e4m3<false>(x[4], x[5], 0u);
+  hi = fp8bs::cvt2_e4m3<true>(x[6], x[7], hi);
+  if (i0 + 8 <= n) {
+    *reinterpret_cast<fp8bs::u32x2*>(codes + i0) = fp8bs::u32x2{lo, hi};
+  } else {
+    for (int j = 0; i0 + j < n; ++j)
+      codes[i0 + j] = (uint8_t)((j < 4 ? lo : hi) >> (8 * (j & 3)));
+  }
+}
+
+}  // namespace
+
+// Returns 0 on success, 2 for a range that is empty, wraps past 0xFFFFFFFF
+// or is too large for one launch, 3 for a misaligned output, or the HIP
+// error of the launch.
+extern "C" int fp8bs_test_convert_range(uint32_t first, int64_t n, uint8_t* codes,
+                                        void* stream) {
+  if (n <= 0 || (uint64_t)first + (uint64_t)n - 1 > 0xFFFFFFFFull || n > (int64_t(1) << 34))
+    return 2;
+  if (reinterpret_cast<uintptr_t>(codes) % 8 != 0) return 3;
+  const int64_t blocks = (n + 2047) / 2048;
+  void* args[] = {&first, &n, &codes};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(convert_range_kernel),
+                              dim3((unsigned)blocks), dim3(256), args, 0,
+                              static_cast<hipStream_t>(stream));
+}

@@ -144,11 +144,12 @@ def test_strided_operands_and_output(fp8bs):
     assert torch.all(OUT[:, 256:] == -1.0)
 
 
-def test_full_size_dense_sampled(fp8bs):
+def test_full_size_dense_all_columns(fp8bs):
     """Dense workload at full size (M=4096, N=18432, K=7168, bf16 out, the
-    launch the benchmark times): GPU quantizers then the GEMM; sampled rows x
-    sampled 128-column blocks are checked against the oracle run on the same
-    bf16 inputs (codes of the sampled rows and bands are also compared)."""
+    launch the benchmark times): GPU quantizers then the GEMM.  The oracle
+    quantizes the whole weight (every code and scale compared) and computes
+    32 rows (0, 127, 128, 255, 4095 and 27 random) over all 18432 columns;
+    every element meets the bare 2e-3 * sum|ab| bar."""
     M, N, K = 4096, 18432, 7168
     a = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
     w = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
@@ -157,22 +158,17 @@ def test_full_size_dense_sampled(fp8bs):
     c = fp8bs.fp8_block_gemm(qa_g, sa_g, qw_g, sw_g, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
-    rows = np.array(sorted(set([0, 127, 128, 255, 4095] + rng.choice(M, 27, replace=False).tolist())))
-    bands = np.array(sorted(set([0, 143] + rng.choice(144, 14, replace=False).tolist())))
-    ab = synth.bf16_bits(a[torch.from_numpy(rows).cuda()])
-    qa, sa = oracle.quant_act_1x128(ab)
+    rows = np.array(sorted(set([0, 127, 128, 255, 4095] +
+                               rng.choice(M, 27, replace=False).tolist())))
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(a[torch.from_numpy(rows).cuda()]))
     gu.assert_same_bits(gu.host(qa_g)[rows], qa, "sampled A codes")
     gu.assert_same_bits(gu.host(sa_g)[:, rows], sa, "sampled A scales")
-    wb_all = w.view(N // 128, 128, K)
-    ch = gu.host_f64(c)
-    worst = 0.0
-    for nb in bands:
-        qw, sw = oracle.quant_w_128x128(synth.bf16_bits(wb_all[nb]))
-        gu.assert_same_bits(gu.host(qw_g[nb * 128:(nb + 1) * 128]), qw, f"band {nb} codes")
-        C, B = oracle.block_gemm(qa, sa, qw, sw)
-        worst = max(worst, gu.check_gemm(ch[rows][:, nb * 128:(nb + 1) * 128], C, B,
-                                          bf16=True))
-    print(f"dense full-size sampled: worst err/bound = {worst:.4f}")
+    qw, sw = oracle.quant_w_128x128(synth.bf16_bits(w))
+    gu.assert_same_bits(gu.host(qw_g), qw, "all W codes")
+    gu.assert_same_bits(gu.host(sw_g), sw, "all W scales")
+    C, B = oracle.block_gemm(qa, sa, qw, sw)
+    worst = gu.check_gemm(gu.host_f64(c)[rows], C, B, bf16=True)
+    gu.report(f"dense 4096x18432x7168 bf16, {len(rows)} rows x all {N} columns", worst)
 
 
 @pytest.mark.parametrize("M", [1, 31, 32, 33, 63, 64, 65])

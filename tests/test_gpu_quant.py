@@ -203,3 +203,42 @@ def test_linear_pair_strided_operands_and_outputs(fp8bs):
     gu.assert_same_bits(gu.host(sw), swr, "weight scales")
     assert torch.all(q_full[:, K:] == 0x5A) and torch.all(qw_full[:, K:] == 0xA5)
     assert torch.all(s_full[:, M:] == -1.0)
+
+
+def test_nonfinite_input_stays_in_its_group(fp8bs):
+    """NaN and infinite inputs are outside the contract and the codes of the
+    group holding one are unspecified; the rest of the tensor must still be
+    the oracle's, bit for bit (activation tiles and weight blocks)."""
+    x = synth.bf16_bits(synth.act(64, 512, case=310, tensor=0)).copy()
+    bad = {(3, 1): 0x7FC0, (9, 0): 0xFFC0, (17, 2): 0x7F81, (40, 3): 0x7F80, (63, 0): 0xFF80}
+    for (m, kb), v in bad.items():
+        x[m, kb * 128 + 17] = v
+    q, s = fp8bs.fp8_quant_act_1x128(gu.bf16_from_bits(x))
+    torch.cuda.synchronize()
+    clean = x.copy()
+    for (m, kb) in bad:
+        clean[m, kb * 128 + 17] = 0
+    qr, sr = oracle.quant_act_1x128(clean)
+    qg, sg = gu.host(q).copy(), gu.host(s).copy()
+    for (m, kb) in bad:
+        qg[m, kb * 128:(kb + 1) * 128] = qr[m, kb * 128:(kb + 1) * 128]
+        sg[kb, m] = sr[kb, m]
+    gu.assert_same_bits(qg, qr, "act codes outside the non-finite tiles")
+    gu.assert_same_bits(sg, sr, "act scales outside the non-finite tiles")
+
+    w = synth.bf16_bits(synth.weight(384, 512, case=311, tensor=1)).copy()
+    w[5, 300] = 0x7FC0   # block (0, 2)
+    w[200, 10] = 0xFF80  # block (1, 0)
+    qw, sw = fp8bs.fp8_quant_w_128x128(gu.bf16_from_bits(w))
+    torch.cuda.synchronize()
+    wc = w.copy()
+    wc[5, 300] = 0
+    wc[200, 10] = 0
+    qwr, swr = oracle.quant_w_128x128(wc)
+    qwg, swg = gu.host(qw).copy(), gu.host(sw).copy()
+    for nb, kb in ((0, 2), (1, 0)):
+        qwg[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128] = \
+            qwr[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128]
+        swg[nb, kb] = swr[nb, kb]
+    gu.assert_same_bits(qwg, qwr, "weight codes outside the non-finite blocks")
+    gu.assert_same_bits(swg, swr, "weight scales outside the non-finite blocks")
