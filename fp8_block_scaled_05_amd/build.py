@@ -32,6 +32,12 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-source additions.  The few-row kernels run one wave per SIMD, where the
+# compiler would put MFMA results in accumulation registers and copy each
+# one out before its FP32 promotion; this option keeps them in VGPRs.
+EXTRA_FLAGS = {"gemm_few_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -48,7 +54,8 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+        cmd = [hipcc, *DEVICE_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

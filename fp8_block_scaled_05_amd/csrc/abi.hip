@@ -147,6 +147,19 @@ int block_gemm_impl(int a_kind, const void* a, int64_t lda, float* sa, int64_t l
   if (out == fp8bs::kOutE4M3 && (!ld_ok(ldc, N) || ldsc < M || !aligned(sc, 4)))
     return FP8BS_ERR_LAYOUT;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16_a = a_kind == FP8BS_A_BF16;
+  if (bf16_a) {
+    // the caller's workspace is required for every bf16-A call (the
+    // few-row path below does not use it)
+    const size_t need = fp8bs_workspace_bytes(FP8BS_OP_GEMM_BF16, M, N, K, 0);
+    if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return FP8BS_ERR_LAYOUT;
+  }
+  if (bf16_a && M <= fp8bs::kFewRowsFused && out != fp8bs::kOutE4M3) {
+    // very few rows: the weight-stream kernel quantizes A itself
+    return hip_status(fp8bs::launch_few_rows_gemm(a, lda, sa, ldsa, true, b, ldb, sb, c, ldc,
+                                                  out == fp8bs::kOutBF16, M, N, K, st));
+  }
 
   fp8bs::GemmArgs g{};
   g.b = b;
@@ -166,9 +179,6 @@ int block_gemm_impl(int a_kind, const void* a, int64_t lda, float* sa, int64_t l
     g.sa = sa;
     g.ldsa = ldsa;
   } else {
-    const size_t need = fp8bs_workspace_bytes(FP8BS_OP_GEMM_BF16, M, N, K, 0);
-    if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return FP8BS_ERR_LAYOUT;
     uint8_t* wq = static_cast<uint8_t*>(workspace);
     float* ws = sa ? sa : reinterpret_cast<float*>(wq + fused_q_bytes(M, K));
     const int64_t wlds = sa ? ldsa : M;
@@ -180,6 +190,10 @@ int block_gemm_impl(int a_kind, const void* a, int64_t lda, float* sa, int64_t l
     g.sa = ws;
     g.ldsa = wlds;
   }
+  if (M <= fp8bs::kFewRows && out != fp8bs::kOutE4M3)
+    return hip_status(fp8bs::launch_few_rows_gemm(g.a, g.lda, const_cast<float*>(g.sa), g.ldsa,
+                                                  false, b, ldb, sb, c, ldc,
+                                                  out == fp8bs::kOutBF16, M, N, K, st));
   return hip_status(fp8bs::launch_block_gemm(g, out, st));
 }
 

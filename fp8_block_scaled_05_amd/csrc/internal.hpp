@@ -90,4 +90,15 @@ hipError_t launch_kgrouped_gemm_rowscaled(const GemmArgs& args, OutKind out,
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, OutKind out, hipStream_t stream);
 
+// Few-row GEMM (M <= kFewRows), fp32 or bf16 output.  fused (M <=
+// kFewRowsFused): A is bf16 [M][lda], quantized per 1x128 tile inside the
+// kernel (sa: optional scale output); otherwise A is E4M3 codes with input
+// scales sa.
+constexpr int64_t kFewRows = 64;
+constexpr int64_t kFewRowsFused = 16;
+hipError_t launch_few_rows_gemm(const void* a, int64_t lda, float* sa, int64_t ldsa, bool fused,
+                                const uint8_t* b, int64_t ldb, const float* sb, void* c,
+                                int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K,
+                                hipStream_t stream);
+
 }  // namespace fp8bs

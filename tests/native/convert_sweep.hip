@@ -12,7 +12,17 @@
 
 namespace {
 
-// codes[i] = E4M3(bits first + i) for i < n; 8 inputs per thread.
+// The convert without the clamp: the few-row GEMM's in-kernel activation
+// quantizer skips the clamp, which changes nothing for finite inputs only if
+// the hardware convert takes every |y| in [448, 464) to the code of 448.
+__device__ __forceinline__ uint32_t cvt2_raw(float a, float b, uint32_t old, bool hi) {
+  return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true)
+            : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+}
+
+// codes[i] = E4M3(bits first + i) for i < n; 8 inputs per thread.  RAW: the
+// bare hardware convert, else the library's clamped cvt2_e4m3.
+template <bool RAW>
 __global__ __launch_bounds__(256) void convert_range_kernel(uint32_t first, int64_t n,
                                                             uint8_t* __restrict__ codes) {
   const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
@@ -21,10 +31,14 @@ __global__ __launch_bounds__(256) void convert_range_kernel(uint32_t first, int6
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     x[j] = i0 + j < n ? __uint_as_float(first + (uint32_t)(i0 + j)) : 0.0f;
-  uint32_t lo = fp8bs::cvt2_e4m3<false>(x[0], x[1], 0u);
-  lo = fp8bs::cvt2_e4m3<true>(x[2], x[3], lo);
-  uint32_t hi = fp8bs::cvt2_e4m3<false>(x[4], x[5], 0u);
-  hi = fp8bs::cvt2_e4m3<true>(x[6], x[7], hi);
+  uint32_t lo, hi;
+  if constexpr (RAW) {
+    lo = cvt2_raw(x[2], x[3], cvt2_raw(x[0], x[1], 0u, false), true);
+    hi = cvt2_raw(x[6], x[7], cvt2_raw(x[4], x[5], 0u, false), true);
+  } else {
+    lo = fp8bs::cvt2_e4m3<true>(x[2], x[3], fp8bs::cvt2_e4m3<false>(x[0], x[1], 0u));
+    hi = fp8bs::cvt2_e4m3<true>(x[6], x[7], fp8bs::cvt2_e4m3<false>(x[4], x[5], 0u));
+  }
   if (i0 + 8 <= n) {
     *reinterpret_cast<fp8bs::u32x2*>(codes + i0) = fp8bs::u32x2{lo, hi};
   } else {
@@ -35,17 +49,19 @@ __global__ __launch_bounds__(256) void convert_range_kernel(uint32_t first, int6
 
 }  // namespace
 
-// Returns 0 on success, 2 for a range that is empty, wraps past 0xFFFFFFFF
-// or is too large for one launch, 3 for a misaligned output, or the HIP
-// error of the launch.
-extern "C" int fp8bs_test_convert_range(uint32_t first, int64_t n, uint8_t* codes,
+// raw != 0: the bare convert (no clamp).  Returns 0 on success, 2 for a
+// range that is empty, wraps past 0xFFFFFFFF or is too large for one launch,
+// 3 for a misaligned output, or the HIP error of the launch.
+extern "C" int fp8bs_test_convert_range(uint32_t first, int64_t n, uint8_t* codes, int raw,
                                         void* stream) {
   if (n <= 0 || (uint64_t)first + (uint64_t)n - 1 > 0xFFFFFFFFull || n > (int64_t(1) << 34))
     return 2;
   if (reinterpret_cast<uintptr_t>(codes) % 8 != 0) return 3;
   const int64_t blocks = (n + 2047) / 2048;
   void* args[] = {&first, &n, &codes};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(convert_range_kernel),
+  const void* k = raw ? reinterpret_cast<const void*>(convert_range_kernel<true>)
+                     : reinterpret_cast<const void*>(convert_range_kernel<false>);
+  return (int)hipLaunchKernel(k,
                               dim3((unsigned)blocks), dim3(256), args, 0,
                               static_cast<hipStream_t>(stream));
 }

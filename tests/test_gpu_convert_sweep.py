@@ -51,14 +51,19 @@ def _oracle_change_points(sign):
     return pts
 
 
-@pytest.mark.parametrize("sign", [0, 1])
-def test_every_float32_value(sign):
+def _lib():
     if not os.path.exists(LIB):
         pytest.fail(f"{LIB} is missing: run python -m fp8_block_scaled_05_amd.build")
     lib = ctypes.CDLL(LIB)
     lib.fp8bs_test_convert_range.restype = ctypes.c_int
     lib.fp8bs_test_convert_range.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p,
-                                             ctypes.c_void_p]
+                                             ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+@pytest.mark.parametrize("sign", [0, 1])
+def test_every_float32_value(sign):
+    lib = _lib()
     base = sign << 31
     stream = torch.cuda.current_stream().cuda_stream
     codes = torch.empty(CHUNK, dtype=torch.uint8, device="cuda")
@@ -67,7 +72,7 @@ def test_every_float32_value(sign):
     total = LAST + 1
     for s0 in range(0, total, CHUNK):
         n = min(CHUNK, total - s0)
-        st = lib.fp8bs_test_convert_range(base + s0, n, codes.data_ptr(), stream)
+        st = lib.fp8bs_test_convert_range(base + s0, n, codes.data_ptr(), 0, stream)
         assert st == 0, f"launch status {st}"
         c = codes[:n]
         first = int(c[0])
@@ -90,3 +95,24 @@ def test_every_float32_value(sign):
     assert not bad, (f"first mismatch at run {bad[0]}: gpu starts at {starts[bad[0]]:#x} with "
                      f"{values[bad[0]]:#x}, oracle {want_starts[bad[0]]:#x} with "
                      f"{want_values[bad[0]]:#x}")
+
+
+@pytest.mark.parametrize("sign", [0, 1])
+def test_bare_convert_rounds_448_to_464_down(sign):
+    """The few-row GEMM's in-kernel activation quantizer converts without the
+    clamp to +-448.  For finite inputs the scaled value never exceeds
+    448.0000534 (every bf16 tile maximum: test_oracle_quant), so that is exact
+    when the bare convert takes every float32 in [448, 464) -- all 2^19 of
+    them -- to the code of 448, as the oracle does (round to nearest even:
+    464 is the midpoint to the first value past the format)."""
+    lib = _lib()
+    first, n = (sign << 31) | 0x43E00000, 0x43E80000 - 0x43E00000   # 448.0 .. 464.0 exclusive
+    codes = torch.empty(n, dtype=torch.uint8, device="cuda")
+    st = lib.fp8bs_test_convert_range(first, n, codes.data_ptr(), 1,
+                                      torch.cuda.current_stream().cuda_stream)
+    assert st == 0, f"launch status {st}"
+    got = codes.cpu().numpy()
+    want = oracle.encode(np.arange(first, first + n, dtype=np.uint32).view(np.float32))
+    assert np.all(want == ((sign << 7) | 0x7E))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first at {first + bad[0]:#x}: {got[bad[0]]:#x}"

@@ -59,7 +59,10 @@ def test_grouped_all_outputs(fp8bs, sizes, N, K, out):
 
 def test_grouped_equals_dense_on_each_slice(fp8bs):
     """Each group's rows through the grouped kernel are bit-identical to the
-    dense kernel on that slice (same per-element arithmetic)."""
+    dense kernel on that slice when the dense call also takes the large-tile
+    kernel (more than 64 rows: same per-element arithmetic).  A slice of at
+    most 64 rows takes the few-row kernel, which adds its K teams' partial
+    sums in another order; it is checked against the oracle instead."""
     sizes = [70, 0, 129, 5, 200]
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     M, N, K = int(offsets[-1]), 256, 512
@@ -72,7 +75,12 @@ def test_grouped_equals_dense_on_each_slice(fp8bs):
         d = fp8bs.fp8_block_gemm(gu.u8(qa[r0:r1]), gu.f32(sa[:, r0:r1]), gu.u8(qw[g]),
                                  gu.f32(sw[g]), out_dtype=torch.float32)
         torch.cuda.synchronize()
-        gu.assert_same_bits(c[r0:r1], gu.host(d), f"group {g}")
+        if r1 - r0 > 64:
+            gu.assert_same_bits(c[r0:r1], gu.host(d), f"group {g}")
+        else:
+            C, B = oracle.block_gemm(qa[r0:r1], sa[:, r0:r1], qw[g], sw[g])
+            gu.check_gemm(gu.host(d), C, B)
+            gu.check_gemm(c[r0:r1], C, B)
 
 
 def test_empty_groups_write_nothing(fp8bs):
