@@ -2,8 +2,17 @@
 // to the gfx950 kernels.  Declarations and the contract are in
 // include/fp8bs.h.
 
+#include <atomic>
+
 #include "fp8bs.h"
 #include "internal.hpp"
+
+// Device buffer of fp8_block_gemm_bf16_noalloc: the E4M3 codes and scales of
+// A quantized inside the call.  Each GPU that loads the library holds its own
+// copy until the process ends.  Host code never uses this name as a device
+// address (on the host it only names the variable); it uses the address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[FP8BS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -244,6 +253,27 @@ fp8bs::OutKind out_of(int out_kind) {
   return out_kind == FP8BS_OUT_BF16 ? fp8bs::kOutBF16 : fp8bs::kOutF32;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.  Concurrent first calls on one
+// device store the same address.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,6 +390,22 @@ int fp8_block_grouped_gemm_e4m3_out(const uint8_t* a, int64_t lda, const float* 
   (void)workspace_bytes;
   return grouped_gemm_impl(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, qc, ldqc,
                            fp8bs::kOutE4M3, sc, ldsc, group_offsets, G, M_total, N, K, stream);
+}
+
+int fp8_block_gemm_bf16_noalloc(const uint16_t* a, int64_t lda, float* sa, int64_t ldsa,
+                                const uint8_t* b, int64_t ldb, const float* sb, void* c,
+                                int64_t ldc, int out_kind, int64_t M, int64_t N, int64_t K,
+                                void* stream) {
+  if (out_kind != FP8BS_OUT_F32 && out_kind != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || K % kTile != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (fp8bs_workspace_bytes(FP8BS_OP_GEMM_BF16, M, N, K, 0) > FP8BS_NOALLOC_SCRATCH_BYTES)
+    return FP8BS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return block_gemm_impl(FP8BS_A_BF16, a, lda, sa, ldsa, b, ldb, sb, c, ldc, out_of(out_kind),
+                         nullptr, 0, M, N, K, ws, FP8BS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t fp8bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t G) {

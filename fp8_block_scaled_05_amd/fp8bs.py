@@ -18,6 +18,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_LAYOUT, ERR_DTYPE, ERR_WORKSPACE, ERR_HIP = range(7
 OUT_F32, OUT_BF16 = 0, 1
 A_E4M3, A_BF16 = 0, 1
 OP_QUANT_ACT, OP_QUANT_W, OP_GEMM_E4M3, OP_GEMM_BF16, OP_GROUPED_GEMM = range(5)
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024  # FP8BS_NOALLOC_SCRATCH_BYTES
 DELAY_TILE, DELAY_TENSOR = 0, 1
 
 EXPORTS = (
@@ -28,6 +29,7 @@ EXPORTS = (
     "fp8_quant_w_128x128_t",
     "fp8_quant_linear",
     "fp8_block_gemm",
+    "fp8_block_gemm_bf16_noalloc",
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_e4m3_out",
     "fp8_block_grouped_gemm_e4m3_out",
@@ -58,6 +60,8 @@ _SIGNATURES = {
                                            _int, _p, _i64, _i64, _i64, _i64, _p], _int),
     "fp8_block_gemm": ([_int, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _int,
                         _i64, _i64, _i64, _p, _sz, _p], _int),
+    "fp8_block_gemm_bf16_noalloc": ([_p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _int, _i64,
+                                     _i64, _i64, _p], _int),
     "fp8_block_grouped_gemm": ([_p, _i64, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _int,
                                 _p, _i64, _i64, _i64, _i64, _p, _sz, _p], _int),
     "fp8_block_gemm_e4m3_out": ([_int, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64,
@@ -450,6 +454,28 @@ def fp8_block_gemm(a, sa, b, sb, out=None, out_dtype=torch.bfloat16, workspace=N
         _check(lib.fp8_block_gemm(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
                                   _ptr(sb), _ptr(out), _ld(out), _out_kind(out.dtype), M, N, K,
                                   _ptr(workspace), ws_bytes, _stream(a)), "fp8_block_gemm")
+    return out
+
+
+def fp8_block_gemm_bf16_noalloc(a, sa, b, sb, out):
+    """``fp8_block_gemm`` with a bf16 ``a`` quantized into the library's own
+    fixed device buffer: the library allocates nothing, and neither does this
+    wrapper (``out`` [M][N] fp32 or bf16 is the caller's; ``sa``
+    [K/128][ldsa], optional, receives the scales).  Calls that overlap on one
+    GPU share that buffer and race."""
+    if a.dtype != torch.bfloat16:
+        raise ValueError("a must be bfloat16")
+    if out is None:
+        raise ValueError("out must be given (this entry point allocates nothing)")
+    _, M, N, K = _dense_operands("fp8_block_gemm_bf16_noalloc", a, sa, b, sb)
+    _mat(out, "out", M, N, out.dtype)
+    _need_device(a, sa, b, sb, out)
+    ldsa = sa.stride(0) if sa is not None else 0
+    with torch.cuda.device(a.device):
+        _check(lib.fp8_block_gemm_bf16_noalloc(_ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
+                                               _ptr(sb), _ptr(out), _ld(out),
+                                               _out_kind(out.dtype), M, N, K, _stream(a)),
+               "fp8_block_gemm_bf16_noalloc")
     return out
 
 

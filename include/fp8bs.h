@@ -260,6 +260,36 @@ int fp8_block_gemm(int a_kind, const void* a, int64_t lda, float* sa,
                    size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fp8_block_gemm with a bf16 A (a_kind FP8BS_A_BF16) whose in-call E4M3
+ * codes and scales go to a fixed device buffer of the library instead of a
+ * caller workspace.  The buffer, FP8BS_NOALLOC_SCRATCH_BYTES bytes, is a
+ * static device array: every GPU that loads the library holds its own copy
+ * until the process ends.  The call allocates nothing (no hipMalloc or
+ * hipFree, no allocating library routine).
+ *
+ *   a       [in]  bf16 [M][lda]; sa [out, may be NULL] fp32 scales
+ *                 sa(m, kb) at sa[kb*ldsa + m], ldsa >= M.
+ *   b, sb, c, ldc, out_kind, M, N, K, stream  as fp8_block_gemm.
+ * Sizes: needs fp8bs_workspace_bytes(FP8BS_OP_GEMM_BF16, M, N, K, 0) <=
+ *   FP8BS_NOALLOC_SCRATCH_BYTES (M <= 1134 rows at K = 7168);
+ *   larger -> FP8BS_ERR_WORKSPACE, before any HIP call.
+ * Sharing: every call on one GPU uses that GPU's one buffer, which keeps the
+ *   last call's contents.  Calls ordered on one stream are safe; calls that
+ *   overlap on one GPU (several streams, or threads without ordering) race
+ *   and give undefined results.
+ * Errors: as fp8_block_gemm (FP8BS_ERR_HIP also if the buffer's device
+ *   address cannot be looked up).
+ */
+#define FP8BS_NOALLOC_SCRATCH_BYTES (8u * 1024u * 1024u)
+int fp8_block_gemm_bf16_noalloc(const uint16_t* a, int64_t lda, float* sa,
+                                int64_t ldsa, const uint8_t* b, int64_t ldb,
+                                const float* sb, void* c, int64_t ldc,
+                                int out_kind, int64_t M, int64_t N, int64_t K,
+                                void* stream);
+
+/*
  * fp8_block_gemm with the output quantized for the next FP8 GEMM: C is
  * computed exactly as by fp8_block_gemm (FP32 accumulator) and then
  * quantized per 1x128 tile along N by the online rule above, inside the

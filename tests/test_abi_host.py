@@ -346,3 +346,24 @@ def test_binding_accepts_empty_operands_with_any_strides(fp8bs):
     x = torch.zeros(256, 0, dtype=torch.bfloat16).t()  # [0][256], column stride 256
     with pytest.raises(ValueError, match="GPU tensors only"):
         fp8bs.fp8_quant_linear(x, torch.zeros(130, 256, dtype=torch.bfloat16))
+
+
+def test_noalloc_gemm_refuses_sizes_beyond_its_buffer(fp8bs):
+    """The allocation-free bf16-A GEMM checks its buffer size before any HIP
+    call (fake pointers; nothing is launched)."""
+    lib = fp8bs.lib
+    K = 7168
+    fits = max(m for m in range(1, 3000)
+               if lib.fp8bs_workspace_bytes(fp8bs.OP_GEMM_BF16, m, 128, K, 0) <=
+               fp8bs.NOALLOC_SCRATCH_BYTES)
+    assert fits == 1134
+
+    def call(M, K=K, out_kind=fp8bs.OUT_BF16):
+        return lib.fp8_block_gemm_bf16_noalloc(P, K, P, M, P, K, P, P, 128, out_kind, M, 128, K,
+                                               None)
+
+    assert call(fits + 1) == fp8bs.ERR_WORKSPACE
+    assert call(100000) == fp8bs.ERR_WORKSPACE
+    assert call(0) == fp8bs.OK
+    assert call(64, K=200) == fp8bs.ERR_SHAPE
+    assert call(64, out_kind=7) == fp8bs.ERR_DTYPE
