@@ -3,29 +3,29 @@
 One step = the whole online-FP8 linear-layer forward on the dense workload:
 quantize the bf16 activations A [4096][7168] per 1x128 tile, quantize the
 bf16 weights W [18432][7168] per 128x128 block (both online, from the current
-values), then the block-scaled FP8 GEMM C = A.W^T with FP32 promotion every
-128 K and bf16 output.  ``value`` is 2*M*N*K / (time per step), in TFLOP/s,
-with all inputs resident in HBM.
+values, in one launch), then the block-scaled FP8 GEMM C = A.W^T with FP32
+promotion every 128 K and bf16 output.  ``value`` is 2*M*N*K / (time per
+step), in TFLOP/s, with all inputs resident in HBM.
 
 The same run also times, outside the timed steps, the other workloads of the
-path: the activation and weight quantizers alone at 8192x7168 / 18432x7168
-(GB/s, buffers rotated past the 256 MB Infinity Cache), the grouped MoE GEMM
-(32 experts, top-8 of 4096 tokens, gate/up and down), the skinny GEMM with
-in-call activation quantization (M = 16, 64), the dense GEMM with its output
-quantized for the next FP8 GEMM (against bf16 output followed by the
-activation quantizer), the backward pass of the dense layer and of the MoE
-gate/up layer (data and weight gradients with their quantizers), online
-against delayed (history-based) scaling on a
-drifting sequence of activations (quantization error, clipped and flushed
-fractions), and the CPU oracle on a bounded sample of the dense step
-(``cpu_baseline``).
+path (``parts``): the activation and weight quantizers alone at 8192x7168 /
+18432x7168 (GB/s, buffers rotated past the 256 MB Infinity Cache) and in one
+launch, a plain HBM copy of the activation quantizer's byte count (the
+streaming reference), the skinny GEMM with bf16 A (M = 16, 64; weights
+rotated), the grouped MoE GEMM (32 experts, top-8 of 4096 tokens, gate/up and
+down), the dense GEMM with its output quantized for the next FP8 GEMM, the
+backward pass of the dense layer and of the MoE gate/up layer, online against
+delayed scaling, and the CPU oracle (``cpu_baseline``).
 
-The default 300 warm-up steps (about 0.2 s) bring the engine clock to its
-sustained level before the timed steps; with only a few warm-up steps the
-first timed GEMMs run at a lower clock.
+Before the W warm-up steps, the step runs until 0.3 s have passed, so that
+the engine clock has settled at the level it holds under this load when the
+timed steps start (with a few warm-up steps alone the first GEMMs run at a
+lower clock).  The engine clock during the timed steps is sampled through
+amdsmi when the library is usable.
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 300] [--no-parts]
        [--no-cpu-baseline]
+       python bench.py --only PART [--iters N]   (one workload, for profiling)
 """
 
 import argparse
@@ -33,6 +33,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +47,7 @@ PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 M, N, K = 4096, 18432, 7168
 GEMM_KERNEL_SOURCES = ("gemm.hip", "gemm_kernel.hpp", "device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_dense_gemm_M4096_N18432_K7168.txt")
+CLOCK_SETTLE_S = 0.3
 
 
 def _parse():
@@ -55,6 +57,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-parts", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="run one part: " + ", ".join(PARTS))
+    ap.add_argument("--iters", type=int, default=30)
     return ap.parse_args()
 
 
@@ -116,32 +120,212 @@ class Timer:
         return ts[len(ts) // 2] if ts else float("nan")
 
 
-def _dense_setup(torch, fp8bs, synth):
+class ClockSampler:
+    """Engine (GFX) clock of GPU 0 sampled through amdsmi in a thread, every
+    ~2 ms; ``window(t0, t1)`` gives the samples taken in [t0, t1].  Unusable
+    amdsmi leaves it empty (the line then carries null)."""
+
+    def __init__(self):
+        self.samples = []
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()  # probe once
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+        except Exception:
+            self._smi = None
+
+    def _read(self):
+        smi, h = self._smi, self._h
+        try:
+            m = smi.amdsmi_get_gpu_metrics_info(h)
+            v = m.get("current_gfxclk")
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                self.source = "amdsmi gpu_metrics current_gfxclk"
+                return float(v)
+            v = m.get("average_gfxclk_frequency")
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                self.source = "amdsmi gpu_metrics average_gfxclk_frequency"
+                return float(v)
+        except Exception:
+            pass
+        c = smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX)
+        self.source = "amdsmi clock_info GFX"
+        return float(c["clk"])
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append((time.perf_counter(), self._read()))
+            except Exception:
+                return
+            time.sleep(0.002)
+
+    def start(self):
+        if self._thread:
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread and self._thread.is_alive():
+            self._thread.join(1.0)
+
+    def window(self, t0, t1):
+        return [v for (t, v) in self.samples if t0 <= t <= t1]
+
+
+def _timeit(torch, fn, iters, warm=5):
+    """Median and p10/p90 (ms) of ``iters`` calls of fn(i) after ``warm``."""
+    tm = Timer(torch)
+    for i in range(warm):
+        fn(i)
+    for i in range(iters):
+        tm.run("x", lambda: fn(i))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in tm.pairs["x"])
+    return ts[len(ts) // 2], ts[len(ts) // 10], ts[(len(ts) * 9) // 10]
+
+
+def _rate(byt, ms):
+    gbps = byt / ms / 1e6
+    return {"GBps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS}
+
+
+def _flops_rate(fl, ms):
+    tf = fl / ms / 1e9
+    return {"TFLOPs": tf, "frac_mfma": tf / PEAK_FP8_TFLOPS}
+
+
+# --------------------------------------------------------------------------
+# Parts: one workload each.  part(ctx, iters) -> dict.  ``ctx`` holds torch,
+# the binding and the input generator.
+
+
+def part_act_quant(c, iters):
+    """Activation quantizer 8192x7168, 4 rotated buffer sets (712 MB)."""
+    torch, fp8bs, synth = c
+    Mq, Kq = 8192, 7168
+    xs = [synth.act(Mq, Kq, case=synth.QUANT.case_id, tensor=i, device="cuda") for i in range(4)]
+    qs = [torch.empty(Mq, Kq, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    ss = [torch.empty(Kq // 128, Mq, dtype=torch.float32, device="cuda") for _ in range(4)]
+    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_quant_act_1x128(xs[i % 4], qs[i % 4],
+                                                                        ss[i % 4]), iters)
+    byt = Mq * Kq * 3.03125
+    return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(byt, med),
+            "bytes": byt}
+
+
+def part_hbm_copy(c, iters):
+    """The streaming reference: torch copy_ of 88,997,888 bytes (4 rotated
+    pairs), which reads and writes the activation quantizer's 177,995,776
+    bytes of HBM traffic in total."""
+    torch, fp8bs, synth = c
+    n = 8192 * 7168 * 3.03125 / 2
+    n = int(n) // 16 * 16
+    src = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i) for i in range(4)]
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    med, p10, p90 = _timeit(torch, lambda i: dst[i % 4].copy_(src[i % 4]), iters)
+    return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(2 * n, med),
+            "bytes": 2 * n}
+
+
+def part_weight_quant(c, iters):
+    """Weight quantizer 18432x7168, 2 rotated sets (793 MB)."""
+    torch, fp8bs, synth = c
+    ws = [synth.weight(N, K, case=synth.QUANT.case_id, tensor=10 + i, device="cuda")
+          for i in range(2)]
+    qws = [torch.empty(N, K, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    sws = [torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda") for _ in range(2)]
+    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_quant_w_128x128(ws[i % 2], qws[i % 2],
+                                                                        sws[i % 2]), iters)
+    byt = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
+    return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(byt, med),
+            "bytes": byt}
+
+
+def part_quant_pair(c, iters):
+    """The quantizer workload as a whole: the 8192x7168 activation and the
+    18432x7168 weight in one launch, 2 rotated sets (1.15 GB)."""
+    torch, fp8bs, synth = c
+    Mq = 8192
+    xs = [synth.act(Mq, K, case=synth.QUANT.case_id, tensor=i, device="cuda") for i in range(2)]
+    ws = [synth.weight(N, K, case=synth.QUANT.case_id, tensor=10 + i, device="cuda")
+          for i in range(2)]
+    out = [(torch.empty(Mq, K, dtype=torch.uint8, device="cuda"),
+            torch.empty(K // 128, Mq, dtype=torch.float32, device="cuda"),
+            torch.empty(N, K, dtype=torch.uint8, device="cuda"),
+            torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda")) for _ in range(2)]
+    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_quant_linear(xs[i % 2], ws[i % 2],
+                                                                     *out[i % 2]), iters)
+    byt = Mq * K * 3.03125 + N * K * 2 + N * K + (N // 128) * (K // 128) * 4
+    return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(byt, med),
+            "bytes": byt}
+
+
+def _skinny(c, iters, Ms):
+    torch, fp8bs, synth = c
+    w = synth.weight(N, K, case=synth.SKINNY.case_id, tensor=1, device="cuda")
+    qw, sw = fp8bs.fp8_quant_w_128x128(w)
+    del w
+    wq = [(qw.clone(), sw.clone()) for _ in range(4)]  # 4 rotated copies: 529 MB
+    x = synth.act(Ms, K, case=synth.SKINNY.case_id, tensor=Ms, device="cuda")
+    cs = torch.empty(Ms, N, dtype=torch.bfloat16, device="cuda")
+    sa_o = torch.empty(K // 128, Ms, dtype=torch.float32, device="cuda")
+    wsp = torch.empty(fp8bs.workspace_bytes(fp8bs.OP_GEMM_BF16, Ms, N, K), dtype=torch.uint8,
+                      device="cuda")
+    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_block_gemm(
+        x, sa_o, wq[i % 4][0], wq[i % 4][1], out=cs, workspace=wsp), iters)
+    byt = N * K + (N // 128) * (K // 128) * 4 + Ms * K * 2 + Ms * N * 2
+    return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(byt, med),
+            "TFLOPs": 2 * Ms * N * K / med / 1e9, "bytes": byt,
+            "activation_quantized": "inside the GEMM kernel" if Ms <= 16 else
+            "by a separate launch before the GEMM"}
+
+
+def part_skinny16(c, iters):
+    """Skinny GEMM, bf16 A M=16 quantized inside the GEMM kernel."""
+    return _skinny(c, iters, 16)
+
+
+def part_skinny64(c, iters):
+    """Skinny GEMM, bf16 A M=64 (quantizer launch, then the few-row GEMM)."""
+    return _skinny(c, iters, 64)
+
+
+def part_dense_gemm(c, iters):
+    """The dense GEMM 4096x18432x7168 alone (bf16 out), the step's operands."""
+    torch, fp8bs, synth = c
     a = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
     w = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
-    qa = torch.empty(M, K, dtype=torch.uint8, device="cuda")
-    sa = torch.empty(K // 128, M, dtype=torch.float32, device="cuda")
-    qw = torch.empty(N, K, dtype=torch.uint8, device="cuda")
-    sw = torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda")
-    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    return a, w, qa, sa, qw, sw, c
+    qa, sa, qw, sw = fp8bs.fp8_quant_linear(a, w)
+    del a, w
+    out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_block_gemm(qa, sa, qw, sw, out=out), iters,
+                            warm=50)
+    return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3,
+            **_flops_rate(2.0 * M * N * K, med)}
 
 
-def _parts(torch, fp8bs, synth, dense, iters=30):
-    import numpy as np
-
-    out = {}
-    tm = Timer(torch)
-
-    # the dense GEMM with its output quantized for the next FP8 GEMM (E4M3
-    # codes + 1x128 scales written by the GEMM), timed interleaved with the
-    # unfused route: bf16 output, then the activation quantizer on it
-    qa, sa, qw, sw = dense
+def part_e4m3_out(c, iters):
+    """The dense GEMM with E4M3 output (the next layer's input), timed
+    interleaved with the unfused route: bf16 output, then the activation
+    quantizer on it."""
+    torch, fp8bs, synth = c
+    a = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
+    w = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
+    qa, sa, qw, sw = fp8bs.fp8_quant_linear(a, w)
+    del a, w
     qc = torch.empty(M, N, dtype=torch.uint8, device="cuda")
     scq = torch.empty(N // 128, M, dtype=torch.float32, device="cuda")
     cb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     qc2 = torch.empty(M, N, dtype=torch.uint8, device="cuda")
     sc2 = torch.empty(N // 128, M, dtype=torch.float32, device="cuda")
+    tm = Timer(torch)
     for i in range(iters + 5):
         f = lambda: fp8bs.fp8_block_gemm_e4m3_out(qa, sa, qw, sw, qc=qc, sc=scq)
         (tm.run("gemm_q", f) if i >= 5 else f())
@@ -149,97 +333,34 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
                       fp8bs.fp8_quant_act_1x128(cb, qc2, sc2))
         (tm.run("gemm_then_q", f2) if i >= 5 else f2())
     ms, ms2 = tm.med_ms("gemm_q"), tm.med_ms("gemm_then_q")
-    out["dense_gemm_e4m3_out_M4096_N18432_K7168"] = {
-        "us": ms * 1e3, "TFLOPs": 2.0 * M * N * K / ms / 1e9,
-        "frac_mfma": 2.0 * M * N * K / ms / 1e9 / PEAK_FP8_TFLOPS,
-        "unfused_bf16_gemm_then_act_quant_us": ms2 * 1e3}
-    del qc, scq, cb, qc2, sc2
-    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, **_flops_rate(2.0 * M * N * K, ms),
+            "unfused_bf16_gemm_then_act_quant_us": ms2 * 1e3}
 
-    # the dense step's operands (4096x7168 activation, 18432x7168 weight):
-    # both quantized in one launch, timed interleaved with two launches
-    a_s = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
-    w_s = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
+
+def part_quant_pair_step(c, iters):
+    """The dense step's operands (4096x7168 activation, 18432x7168 weight):
+    both quantized in one launch, timed interleaved with two launches."""
+    torch, fp8bs, synth = c
+    a = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
+    w = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
+    qa, sa, qw, sw = fp8bs.fp8_quant_linear(a, w)
+    tm = Timer(torch)
     for i in range(iters + 5):
-        f = lambda: fp8bs.fp8_quant_linear(a_s, w_s, qa, sa, qw, sw)
+        f = lambda: fp8bs.fp8_quant_linear(a, w, qa, sa, qw, sw)
         (tm.run("q_pair", f) if i >= 5 else f())
-        f2 = lambda: (fp8bs.fp8_quant_act_1x128(a_s, qa, sa),
-                      fp8bs.fp8_quant_w_128x128(w_s, qw, sw))
+        f2 = lambda: (fp8bs.fp8_quant_act_1x128(a, qa, sa), fp8bs.fp8_quant_w_128x128(w, qw, sw))
         (tm.run("q_two", f2) if i >= 5 else f2())
     ms, ms2 = tm.med_ms("q_pair"), tm.med_ms("q_two")
     byt = M * K * 3.03125 + N * K * (3.0 + 4.0 / 16384)
-    out["quant_pair_one_launch_4096x7168_and_18432x7168"] = {
-        "us": ms * 1e3, "GBps": byt / ms / 1e6, "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
-        "two_launches_us": ms2 * 1e3}
-    del a_s, w_s
-    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, **_rate(byt, ms), "two_launches_us": ms2 * 1e3}
 
-    # activation quantizer 8192x7168, 4 rotated buffer sets (712 MB)
-    Mq, Kq = 8192, 7168
-    xs = [synth.act(Mq, Kq, case=synth.QUANT.case_id, tensor=i, device="cuda") for i in range(4)]
-    qs = [torch.empty(Mq, Kq, dtype=torch.uint8, device="cuda") for _ in range(4)]
-    ss = [torch.empty(Kq // 128, Mq, dtype=torch.float32, device="cuda") for _ in range(4)]
-    for i in range(iters + 5):
-        j = i % 4
-        f = lambda: fp8bs.fp8_quant_act_1x128(xs[j], qs[j], ss[j])
-        (tm.run("qa", f) if i >= 5 else f())
-    ms = tm.med_ms("qa")
-    byt = Mq * Kq * 3.03125
-    out["act_quant_8192x7168"] = {"us": ms * 1e3, "GBps": byt / ms / 1e6,
-                                  "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
-                                  "bytes": byt}
 
-    # weight quantizer 18432x7168, 2 rotated sets (793 MB)
-    ws = [synth.weight(N, K, case=synth.QUANT.case_id, tensor=10 + i, device="cuda") for i in range(2)]
-    qws = [torch.empty(N, K, dtype=torch.uint8, device="cuda") for _ in range(2)]
-    sws = [torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda") for _ in range(2)]
-    for i in range(iters + 5):
-        j = i % 2
-        f = lambda: fp8bs.fp8_quant_w_128x128(ws[j], qws[j], sws[j])
-        (tm.run("qw", f) if i >= 5 else f())
-    ms = tm.med_ms("qw")
-    byt = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
-    out["weight_quant_18432x7168"] = {"us": ms * 1e3, "GBps": byt / ms / 1e6,
-                                      "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS, "bytes": byt}
-
-    # the quantizer workload as a whole: the 8192x7168 activation and the
-    # 18432x7168 weight in one launch, 2 rotated sets (1.15 GB)
-    for i in range(iters + 5):
-        j = i % 2
-        f = lambda: fp8bs.fp8_quant_linear(xs[j], ws[j], qs[j], ss[j], qws[j], sws[j])
-        (tm.run("qpair", f) if i >= 5 else f())
-    ms = tm.med_ms("qpair")
-    byt = Mq * Kq * 3.03125 + byt
-    out["quant_pair_8192x7168_and_18432x7168"] = {
-        "us": ms * 1e3, "GBps": byt / ms / 1e6, "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
-        "bytes": byt}
-    del xs, qs, ss
-    torch.cuda.empty_cache()
-
-    # skinny GEMM with in-call activation quantization, W rotated over 4 copies
-    wq = [(qws[i % 2].clone(), sws[i % 2].clone()) for i in range(4)]
-    del ws, qws, sws
-    for Ms in (16, 64):
-        x = synth.act(Ms, K, case=synth.SKINNY.case_id, tensor=Ms, device="cuda")
-        cs = torch.empty(Ms, N, dtype=torch.bfloat16, device="cuda")
-        sa_o = torch.empty(K // 128, Ms, dtype=torch.float32, device="cuda")
-        wsp = torch.empty(fp8bs.workspace_bytes(fp8bs.OP_GEMM_BF16, Ms, N, K), dtype=torch.uint8,
-                          device="cuda")
-        name = f"skinny{Ms}"
-        for i in range(iters + 5):
-            q, s = wq[i % 4]
-            f = lambda: fp8bs.fp8_block_gemm(x, sa_o, q, s, out=cs, workspace=wsp)
-            (tm.run(name, f) if i >= 5 else f())
-        ms = tm.med_ms(name)
-        byt = N * K + (N // 128) * (K // 128) * 4 + Ms * K * 2 + Ms * N * 2
-        out[f"skinny_fused_M{Ms}_N18432_K7168"] = {
-            "us": ms * 1e3, "GBps": byt / ms / 1e6, "frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS,
-            "TFLOPs": 2 * Ms * N * K / ms / 1e9, "bytes": byt}
-    del wq
-    torch.cuda.empty_cache()
-
-    # grouped MoE: 4096 tokens, top-8 of 32 experts; gate/up N=4096 K=7168,
-    # down N=7168 K=2048; step = quantize A's and all expert weights + 2 GEMMs
+def part_moe(c, iters):
+    """Grouped MoE: 4096 tokens, top-8 of 32 experts; gate/up N=4096 K=7168,
+    down N=7168 K=2048; step = quantize the A's and all expert weights, then
+    the two grouped GEMMs."""
+    import numpy as np
+    torch, fp8bs, synth = c
     G, T = 32, 4096
     order, offsets = synth.routing(T, G, 8, case=synth.MOE.case_id)
     Mt = int(offsets[-1])
@@ -260,6 +381,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
     sw2 = torch.empty(G, 56, 16, dtype=torch.float32, device="cuda")
     c1 = torch.empty(Mt, 4096, dtype=torch.bfloat16, device="cuda")
     c2 = torch.empty(Mt, 7168, dtype=torch.bfloat16, device="cuda")
+    tm = Timer(torch)
 
     def moe_step(timed):
         run = tm.run if timed else (lambda n, f: f())
@@ -277,31 +399,43 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
 
     for i in range(3):
         moe_step(False)
-    for i in range(10):
+    for i in range(max(iters // 3, 5)):
         moe_step(True)
     f1 = 2.0 * Mt * 4096 * 7168
     f2 = 2.0 * Mt * 7168 * 2048
     g1, g2 = tm.med_ms("moe_g1"), tm.med_ms("moe_g2")
     tot = g1 + g2 + tm.med_ms("moe_qa") + tm.med_ms("moe_qw")
-    out["moe_grouped_E32_top8_T4096"] = {
-        "M_total": Mt, "experts_empty": int((offsets[1:] == offsets[:-1]).sum()),
-        "gate_up_us": g1 * 1e3, "gate_up_TFLOPs": f1 / g1 / 1e9,
-        "down_us": g2 * 1e3, "down_TFLOPs": f2 / g2 / 1e9,
-        "gemms_TFLOPs": (f1 + f2) / (g1 + g2) / 1e9,
-        "gemms_frac_mfma": (f1 + f2) / (g1 + g2) / 1e9 / PEAK_FP8_TFLOPS,
-        "step_with_quant_us": tot * 1e3, "step_TFLOPs": (f1 + f2) / tot / 1e9}
-    del a2, w2, qa2, sa2, qw2, sw2, c2, c1
+    return {"M_total": Mt, "experts_empty": int((offsets[1:] == offsets[:-1]).sum()),
+            "gate_up_us": g1 * 1e3, "gate_up_TFLOPs": f1 / g1 / 1e9,
+            "down_us": g2 * 1e3, "down_TFLOPs": f2 / g2 / 1e9,
+            "gemms_TFLOPs": (f1 + f2) / (g1 + g2) / 1e9,
+            "gemms_frac_mfma": (f1 + f2) / (g1 + g2) / 1e9 / PEAK_FP8_TFLOPS,
+            "step_with_quant_us": tot * 1e3, "step_TFLOPs": (f1 + f2) / tot / 1e9}
 
-    # MoE backward of the gate/up layer (same routing): data gradient
-    # dX = dY . W_g (grouped GEMM over per-expert transposed weights) and
-    # weight gradients dW_g = dY_g^T . X_g (one launch over the experts'
-    # 128-padded token ranges)
+
+def part_moe_backward(c, iters):
+    """MoE backward of the gate/up layer (same routing): data gradient
+    dX = dY . W_g (grouped GEMM over per-expert transposed weights) and
+    weight gradients dW_g = dY_g^T . X_g (one launch over the experts'
+    128-padded token ranges)."""
+    import numpy as np
+    torch, fp8bs, synth = c
+    G, T = 32, 4096
+    order, offsets = synth.routing(T, G, 8, case=synth.MOE.case_id)
+    Mt = int(offsets[-1])
+    off_d = torch.from_numpy(offsets).cuda()
+    tokens = synth.act(T, 7168, case=synth.MOE.case_id, tensor=0, device="cuda")
+    a1 = tokens[torch.from_numpy(order).cuda()]
+    del tokens
+    w1 = synth.expert_weights(G, 4096, 7168, case=synth.MOE.case_id, tensor=10, device="cuda")
     dy1 = synth.act(Mt, 4096, case=synth.MOE.case_id, tensor=2, device="cuda")
     qwt = torch.empty(G, 7168, 4096, dtype=torch.uint8, device="cuda")
     swt = torch.empty(G, 56, 32, dtype=torch.float32, device="cuda")
     for g in range(G):
-        fp8bs.fp8_quant_w_128x128_t(w1[g], qw1[g], sw1[g], qwt[g], swt[g])
-    del w1, qw1, sw1
+        _, _, qt, st = fp8bs.fp8_quant_w_128x128_t(w1[g])
+        qwt[g].copy_(qt)
+        swt[g].copy_(st)
+    del w1
     sizes = offsets[1:] - offsets[:-1]
     poff = np.concatenate([[0], np.cumsum((sizes + 127) // 128 * 128)]).astype(np.int32)
     Tp = int(poff[-1])
@@ -321,6 +455,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
     sxt = torch.empty(Tp // 128, 7168, dtype=torch.float32, device="cuda")
     dw1 = torch.empty(G, 4096, 7168, dtype=torch.float32, device="cuda")
     dw1b = torch.empty(G, 4096, 7168, dtype=torch.bfloat16, device="cuda")
+    tm = Timer(torch)
 
     def moe_bwd(timed):
         run = tm.run if timed else (lambda n, f: f())
@@ -335,25 +470,26 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
 
     for i in range(3):
         moe_bwd(False)
-    for i in range(10):
+    for i in range(max(iters // 3, 5)):
         moe_bwd(True)
     fdx = 2.0 * Mt * 4096 * 7168
     fdw = 2.0 * Tp * 4096 * 7168  # padded tokens included (zero rows)
     tdx, tdw, tq = tm.med_ms("mb_dx"), tm.med_ms("mb_dw"), tm.med_ms("mb_q")
-    out["moe_backward_gate_up_E32_top8_T4096"] = {
-        "tokens_padded": Tp,
-        "dgrad_us": tdx * 1e3, "dgrad_TFLOPs": fdx / tdx / 1e9,
-        "wgrad_us": tdw * 1e3, "wgrad_TFLOPs": fdw / tdw / 1e9,
-        "wgrad_useful_TFLOPs": fdx / tdw / 1e9,
-        "wgrad_bf16_out_us": tm.med_ms("mb_dw16") * 1e3,
-        "wgrad_bf16_out_TFLOPs": fdw / tm.med_ms("mb_dw16") / 1e9,
-        "quantizers_us": tq * 1e3}
-    del dy1, qwt, swt, dyp, xp, qdy1, sdy1, dx1, qdyt, sdyt, qxt, sxt, dw1, dw1b, a1
-    torch.cuda.empty_cache()
+    return {"tokens_padded": Tp,
+            "dgrad_us": tdx * 1e3, "dgrad_TFLOPs": fdx / tdx / 1e9,
+            "wgrad_us": tdw * 1e3, "wgrad_TFLOPs": fdw / tdw / 1e9,
+            "wgrad_useful_TFLOPs": fdx / tdw / 1e9,
+            "wgrad_bf16_out_us": tm.med_ms("mb_dw16") * 1e3,
+            "wgrad_bf16_out_TFLOPs": fdw / tm.med_ms("mb_dw16") / 1e9,
+            "quantizers_us": tq * 1e3}
 
-    # backward pass of the dense layer (tokens 4096, N=18432, K=7168):
-    # quantizers with transposed outputs, data gradient dX = dY . W
-    # (contraction 18432) and weight gradient dW = dY^T . X (contraction 4096)
+
+def part_backward(c, iters):
+    """Backward pass of the dense layer (tokens 4096, N=18432, K=7168):
+    quantizers with transposed outputs, data gradient dX = dY . W
+    (contraction 18432) and weight gradient dW = dY^T . X (contraction
+    4096)."""
+    torch, fp8bs, synth = c
     Mb = M
     dy = synth.act(Mb, N, case=synth.DENSE.case_id, tensor=20, device="cuda")
     xb = synth.act(Mb, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
@@ -370,6 +506,7 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
     sxt = torch.empty(Mb // 128, K, dtype=torch.float32, device="cuda")
     dx = torch.empty(Mb, K, dtype=torch.bfloat16, device="cuda")
     dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    tm = Timer(torch)
 
     def bwd(timed):
         run = tm.run if timed else (lambda n, f: f())
@@ -384,24 +521,84 @@ def _parts(torch, fp8bs, synth, dense, iters=30):
         bwd(i >= 5)
     fl = 2.0 * Mb * N * K
     t = {k: tm.med_ms(k) for k in ("b_qw", "b_qdy", "b_qdyt", "b_qxt", "b_dx", "b_dw")}
-    out["backward_dense_M4096_N18432_K7168"] = {
-        "weight_quant_with_transpose_us": t["b_qw"] * 1e3,
-        "weight_quant_with_transpose_GBps": N * K * 4 / t["b_qw"] / 1e6,
-        "dy_quant_1x128_us": t["b_qdy"] * 1e3,
-        "dy_quant_128x1_t_us": t["b_qdyt"] * 1e3,
-        "dy_quant_128x1_t_GBps": Mb * N * 3.03125 / t["b_qdyt"] / 1e6,
-        "x_quant_128x1_t_us": t["b_qxt"] * 1e3,
-        "dgrad_us": t["b_dx"] * 1e3, "dgrad_TFLOPs": fl / t["b_dx"] / 1e9,
-        "dgrad_frac_mfma": fl / t["b_dx"] / 1e9 / PEAK_FP8_TFLOPS,
-        "wgrad_us": t["b_dw"] * 1e3, "wgrad_TFLOPs": fl / t["b_dw"] / 1e9,
-        "wgrad_frac_mfma": fl / t["b_dw"] / 1e9 / PEAK_FP8_TFLOPS,
-        "step_us": sum(t.values()) * 1e3}
-    del dy, xb, wb, bq, bs, bqt, bst, qdy, sdy, qdyt, sdyt, qxt, sxt, dx, dw
-    torch.cuda.empty_cache()
+    return {"weight_quant_with_transpose_us": t["b_qw"] * 1e3,
+            "weight_quant_with_transpose_GBps": N * K * 4 / t["b_qw"] / 1e6,
+            "dy_quant_1x128_us": t["b_qdy"] * 1e3,
+            "dy_quant_128x1_t_us": t["b_qdyt"] * 1e3,
+            "dy_quant_128x1_t_GBps": Mb * N * 3.03125 / t["b_qdyt"] / 1e6,
+            "x_quant_128x1_t_us": t["b_qxt"] * 1e3,
+            "dgrad_us": t["b_dx"] * 1e3, "dgrad_TFLOPs": fl / t["b_dx"] / 1e9,
+            "dgrad_frac_mfma": fl / t["b_dx"] / 1e9 / PEAK_FP8_TFLOPS,
+            "wgrad_us": t["b_dw"] * 1e3, "wgrad_TFLOPs": fl / t["b_dw"] / 1e9,
+            "wgrad_frac_mfma": fl / t["b_dw"] / 1e9 / PEAK_FP8_TFLOPS,
+            "step_us": sum(t.values()) * 1e3}
 
-    # online vs delayed scaling on drifting activations (quality, not speed)
+
+def part_tiny(c, iters):
+    """The tiny workload: quantize A 128x512 and W 256x512, GEMM with fp32
+    output (launch-latency bound)."""
+    torch, fp8bs, synth = c
+    a, w = synth.tiny_inputs(device="cuda")
+    out = torch.empty(128, 256, dtype=torch.float32, device="cuda")
+
+    def f(i):
+        qa, sa = fp8bs.fp8_quant_act_1x128(a)
+        qw, sw = fp8bs.fp8_quant_w_128x128(w)
+        fp8bs.fp8_block_gemm(qa, sa, qw, sw, out=out)
+
+    med, p10, p90 = _timeit(torch, f, iters)
+    return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3,
+            "note": "three launches (act quant, weight quant, GEMM) and the binding's tensor "
+                    "allocations; latency bound"}
+
+
+def part_ablation(c, iters):
+    """Online against delayed scaling on drifting activations (quality)."""
     from fp8_block_scaled_05_amd import ablation
-    out["online_vs_delayed_scaling_M4096_K7168"] = ablation.run(steps=24, timing_iters=10)
+    return ablation.run(steps=24, timing_iters=10)
+
+
+PARTS = {
+    "dense_gemm": part_dense_gemm,
+    "e4m3_out": part_e4m3_out,
+    "quant_pair_step": part_quant_pair_step,
+    "act_quant": part_act_quant,
+    "hbm_copy": part_hbm_copy,
+    "weight_quant": part_weight_quant,
+    "quant_pair": part_quant_pair,
+    "skinny16": part_skinny16,
+    "skinny64": part_skinny64,
+    "moe": part_moe,
+    "moe_backward": part_moe_backward,
+    "backward": part_backward,
+    "tiny": part_tiny,
+    "ablation": part_ablation,
+}
+
+# keys of the parts in the bench line (named for their workloads)
+PART_KEYS = {
+    "e4m3_out": "dense_gemm_e4m3_out_M4096_N18432_K7168",
+    "quant_pair_step": "quant_pair_one_launch_4096x7168_and_18432x7168",
+    "act_quant": "act_quant_8192x7168",
+    "hbm_copy": "hbm_copy_reference_177995776_bytes",
+    "weight_quant": "weight_quant_18432x7168",
+    "quant_pair": "quant_pair_8192x7168_and_18432x7168",
+    "skinny16": "skinny_bf16_act_M16_N18432_K7168",
+    "skinny64": "skinny_bf16_act_M64_N18432_K7168",
+    "moe": "moe_grouped_E32_top8_T4096",
+    "moe_backward": "moe_backward_gate_up_E32_top8_T4096",
+    "backward": "backward_dense_M4096_N18432_K7168",
+    "tiny": "tiny_M128_N256_K512",
+    "ablation": "online_vs_delayed_scaling_M4096_K7168",
+}
+
+
+def _parts(ctx, iters=30):
+    torch = ctx[0]
+    out = {}
+    for name, key in PART_KEYS.items():
+        out[key] = PARTS[name](ctx, iters)
+        torch.cuda.empty_cache()
     return out
 
 
@@ -413,31 +610,80 @@ def _rounded(v):
     return v
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _cpu_baseline():
-    """The oracle, as it stands, on a bounded sample of the dense step: the
-    same N and K, 2048 of the 4096 rows of A (about 10-15 s on 16 cores)."""
+    """The oracle, as it stands, on the machine's host cores: the quantizer
+    workload's two tensors in full (GB/s), the tiny workload in full, and
+    the dense GEMM on 1024 of its 4096 rows (the metric's TFLOP/s; N and K
+    full), about 25 s in all."""
     import numpy as np
 
     import oracle
     from fp8_block_scaled_05_amd import synth
 
-    Ms, Ns = 2048, N
-    a = synth.bf16_bits(synth.act(Ms, K, case=synth.DENSE.case_id, tensor=50))
-    w = synth.bf16_bits(synth.weight(Ns, K, case=synth.DENSE.case_id, tensor=51))
+    res = {}
+    # tiny workload in full
+    a, w = synth.tiny_inputs()
     t0 = time.perf_counter()
-    qa, sa = oracle.quant_act_1x128(a)
-    qw, sw = oracle.quant_w_128x128(w)
+    qa, sa = oracle.quant_act_1x128(synth.bf16_bits(a))
+    qw, sw = oracle.quant_w_128x128(synth.bf16_bits(w))
     oracle.block_gemm(qa, sa, qw, sw)
-    dt = time.perf_counter() - t0
+    res["tiny_full_s"] = time.perf_counter() - t0
+    # quantizers on the full 8192x7168 activation and 18432x7168 weight
+    x = synth.bf16_bits(synth.act(8192, K, case=synth.QUANT.case_id, tensor=0))
+    t0 = time.perf_counter()
+    oracle.quant_act_1x128(x)
+    dt_a = time.perf_counter() - t0
+    res["act_quant_8192x7168_GBps"] = 8192 * K * 3.03125 / dt_a / 1e9
+    del x
+    wb = synth.bf16_bits(synth.weight(N, K, case=synth.QUANT.case_id, tensor=10))
+    t0 = time.perf_counter()
+    qw, sw = oracle.quant_w_128x128(wb)
+    dt_w = time.perf_counter() - t0
+    res["weight_quant_18432x7168_GBps"] = N * K * (3.0 + 4.0 / 16384) / dt_w / 1e9
+    del wb
+    # dense GEMM on a row sample, float64 per-group sums
+    Ms = 1024
+    qa, sa = oracle.quant_act_1x128(
+        synth.bf16_bits(synth.act(Ms, K, case=synth.DENSE.case_id, tensor=50)))
+    t0 = time.perf_counter()
+    oracle.block_gemm(qa, sa, qw, sw)
+    dt_g = time.perf_counter() - t0
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    return {"value": 2.0 * Ms * Ns * K / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+        blas = None
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 2.0 * Ms * N * K / dt_g / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"dense step (1x128 act quant, 128x128 weight quant, float64 block GEMM) "
-                      f"on M={Ms}, N={Ns}, K={K}: {dt:.2f} s"}
+            "sample": f"block GEMM (float64 per-group sums) on M={Ms} of the dense workload's "
+                      f"4096 rows, N={N}, K={K}: {dt_g:.2f} s; also the act quantizer on the full "
+                      f"8192x7168 ({dt_a:.2f} s) and the weight quantizer on the full 18432x7168 "
+                      f"({dt_w:.2f} s), and the tiny workload in full",
+            "cpu_model": _cpu_model(), "blas_threads": blas,
+            "quantizers_and_tiny": _rounded(res)}
+
+
+def _only(args):
+    import torch
+
+    from fp8_block_scaled_05_amd import fp8bs, synth
+    if args.only not in PARTS:
+        print(f"unknown part {args.only}; parts: {', '.join(PARTS)}", file=sys.stderr)
+        sys.exit(2)
+    res = PARTS[args.only]((torch, fp8bs, synth), args.iters)
+    print(json.dumps({"part": args.only, "iters": args.iters, **_rounded(res)}), flush=True)
 
 
 def main():
@@ -447,12 +693,21 @@ def main():
               "sharding of this path is a design note, not a measured configuration.",
               file=sys.stderr)
         sys.exit(2)
+    if args.only:
+        _only(args)
+        return
 
     import torch
 
     from fp8_block_scaled_05_amd import fp8bs, synth
 
-    a, w, qa, sa, qw, sw, c = _dense_setup(torch, fp8bs, synth)
+    a = synth.act(M, K, case=synth.DENSE.case_id, tensor=0, device="cuda")
+    w = synth.weight(N, K, case=synth.DENSE.case_id, tensor=1, device="cuda")
+    qa = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(K // 128, M, dtype=torch.float32, device="cuda")
+    qw = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    sw = torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda")
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     tm = Timer(torch)
 
     def step(timed):
@@ -460,6 +715,16 @@ def main():
         run("quant", lambda: fp8bs.fp8_quant_linear(a, w, qa, sa, qw, sw))
         run("gemm", lambda: fp8bs.fp8_block_gemm(qa, sa, qw, sw, out=c))
 
+    clock = ClockSampler()
+    clock.start()
+    # settle the engine clock, then the W warm-up steps
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < CLOCK_SETTLE_S:
+        for _ in range(20):
+            step(False)
+        settle_steps += 20
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -468,6 +733,8 @@ def main():
         step(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock.stop()
+    clk = clock.window(t0, t1)
     ms_step = (t1 - t0) * 1e3 / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
@@ -479,6 +746,7 @@ def main():
     # algorithmic bytes of the one-launch quantizer pair: bf16 in, codes and
     # scales out, for the activation (1x128 tiles) and the weight (128x128)
     quant_bytes = M * K * 3.03125 + N * K * (3.0 + 4.0 / 16384)
+    clock_mhz = sorted(clk)[len(clk) // 2] if clk else None
 
     line = {
         "metric": METRIC,
@@ -503,13 +771,20 @@ def main():
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic, "kernel": "block_gemm_kernel",
                      "kernel_us": round(g_ms * 1e3, 2)},
+        "clock": {"engine_mhz_timed_median": clock_mhz,
+                  "samples_in_timed_steps": len(clk), "source": clock.source,
+                  "settle_s": CLOCK_SETTLE_S, "settle_steps": settle_steps,
+                  "peak_at_held_clock_TFLOPs": (round(PEAK_FP8_TFLOPS * clock_mhz / 2400.0, 1)
+                                                if clock_mhz else None)},
         "breakdown_us": {"quant_act_and_weight": round(q_ms * 1e3, 2),
                          "gemm": round(g_ms * 1e3, 2)},
         "quant_in_step": {"GBps": round(quant_bytes / q_ms / 1e6, 1),
                           "frac_hbm": round(quant_bytes / q_ms / 1e6 / PEAK_HBM_GBPS, 4)},
     }
+    del a, w, c
+    torch.cuda.empty_cache()
     if not args.no_parts:
-        line["parts"] = _rounded(_parts(torch, fp8bs, synth, (qa, sa, qw, sw)))
+        line["parts"] = _rounded(_parts((torch, fp8bs, synth)))
     line["cpu_baseline"] = None if args.no_cpu_baseline else _cpu_baseline()
     print(json.dumps(line), flush=True)
 
