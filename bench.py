@@ -46,7 +46,7 @@ PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 
 M, N, K = 4096, 18432, 7168
 GEMM_KERNEL_SOURCES = ("gemm.hip", "gemm_kernel.hpp", "device.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_dense_gemm_M4096_N18432_K7168.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_dense_gemm.txt")
 CLOCK_SETTLE_S = 0.3
 
 
