@@ -20,8 +20,9 @@ delayed scaling, and the CPU oracle (``cpu_baseline``).
 Before the W warm-up steps, the step runs until 0.3 s have passed, so that
 the engine clock has settled at the level it holds under this load when the
 timed steps start (with a few warm-up steps alone the first GEMMs run at a
-lower clock).  The engine clock during the timed steps is sampled through
-amdsmi when the library is usable.
+lower clock).  The line reports the engine clock of each XCD averaged over
+the timed steps, from cycle-counter and wall-clock stamps taken on the GPU
+just before and after them (tests/native/clock_probe.hip).
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 300] [--no-parts]
        [--no-cpu-baseline]
@@ -33,7 +34,6 @@ import hashlib
 import json
 import os
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -120,63 +120,59 @@ class Timer:
         return ts[len(ts) // 2] if ts else float("nan")
 
 
-class ClockSampler:
-    """Engine (GFX) clock of GPU 0 sampled through amdsmi in a thread, every
-    ~2 ms; ``window(t0, t1)`` gives the samples taken in [t0, t1].  Unusable
-    amdsmi leaves it empty (the line then carries null)."""
+class ClockStamps:
+    """Average engine clock of each XCD over a stretch of GPU work, from the
+    cycle counter and the constant-rate wall clock that a small kernel stamps
+    before and after it (tests/native/clock_probe.hip: clock64 counts at the
+    XCD's engine clock, wall_clock64 at the rate the runtime reports).  The
+    firmware metrics that SMI tools read lag the load by about 0.4 s, longer
+    than the timed steps.  Without the helper library the line carries null."""
 
-    def __init__(self):
-        self.samples = []
-        self.source = None
-        self._stop = threading.Event()
-        self._thread = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self._smi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handles()[0]
-            self._read()  # probe once
-            self._thread = threading.Thread(target=self._loop, daemon=True)
-        except Exception:
-            self._smi = None
+    BLOCKS = 2048  # 8 per compute unit, so that both stamps reach every one
+    LIB = os.path.join(ROOT, "tests", "native", "libclock_probe.so")
 
-    def _read(self):
-        smi, h = self._smi, self._h
-        try:
-            m = smi.amdsmi_get_gpu_metrics_info(h)
-            v = m.get("current_gfxclk")
-            if isinstance(v, (int, float)) and 0 < v < 10000:
-                self.source = "amdsmi gpu_metrics current_gfxclk"
-                return float(v)
-            v = m.get("average_gfxclk_frequency")
-            if isinstance(v, (int, float)) and 0 < v < 10000:
-                self.source = "amdsmi gpu_metrics average_gfxclk_frequency"
-                return float(v)
-        except Exception:
-            pass
-        c = smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX)
-        self.source = "amdsmi clock_info GFX"
-        return float(c["clk"])
+    def __init__(self, torch):
+        import ctypes
 
-    def _loop(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append((time.perf_counter(), self._read()))
-            except Exception:
-                return
-            time.sleep(0.002)
+        self.torch = torch
+        self.lib = None
+        if os.path.exists(self.LIB):
+            lib = ctypes.CDLL(self.LIB)
+            lib.fp8bs_clock_stamp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+            lib.fp8bs_clock_stamp.restype = ctypes.c_int
+            lib.fp8bs_wall_clock_khz.restype = ctypes.c_int
+            self.khz = lib.fp8bs_wall_clock_khz()
+            if self.khz > 0:
+                self.lib = lib
+        self.bufs = [torch.zeros(3 * self.BLOCKS, dtype=torch.int64, device="cuda")
+                     for _ in range(2)]
 
-    def start(self):
-        if self._thread:
-            self._thread.start()
+    def stamp(self, i):
+        if self.lib is not None:
+            st = self.torch.cuda.current_stream().cuda_stream
+            if self.lib.fp8bs_clock_stamp(self.bufs[i].data_ptr(), self.BLOCKS, st) != 0:
+                self.lib = None
 
-    def stop(self):
-        self._stop.set()
-        if self._thread and self._thread.is_alive():
-            self._thread.join(1.0)
-
-    def window(self, t0, t1):
-        return [v for (t, v) in self.samples if t0 <= t <= t1]
+    def mhz(self):
+        """{xcc: MHz}, the median over the XCD's compute units of each unit's
+        cycles / wall time between its earliest stamp in launch 0 and its
+        latest in launch 1; None without the helper."""
+        if self.lib is None:
+            return None
+        self.torch.cuda.synchronize()
+        first, last = {}, {}
+        for key, cyc, wall in self.bufs[0].view(self.BLOCKS, 3).cpu().tolist():
+            if key not in first or wall < first[key][1]:
+                first[key] = (cyc, wall)
+        for key, cyc, wall in self.bufs[1].view(self.BLOCKS, 3).cpu().tolist():
+            if key not in last or wall > last[key][1]:
+                last[key] = (cyc, wall)
+        per_xcc = {}
+        for key in first.keys() & last.keys():
+            (c0, w0), (c1, w1) = first[key], last[key]
+            if w1 > w0:
+                per_xcc.setdefault(key // 256, []).append((c1 - c0) / (w1 - w0) * self.khz / 1e3)
+        return {x: sorted(v)[len(v) // 2] for x, v in sorted(per_xcc.items())} or None
 
 
 def _timeit(torch, fn, iters, warm=5):
@@ -715,8 +711,7 @@ def main():
         run("quant", lambda: fp8bs.fp8_quant_linear(a, w, qa, sa, qw, sw))
         run("gemm", lambda: fp8bs.fp8_block_gemm(qa, sa, qw, sw, out=c))
 
-    clock = ClockSampler()
-    clock.start()
+    clock = ClockStamps(torch)
     # settle the engine clock, then the W warm-up steps
     settle_steps = 0
     t_settle = time.perf_counter()
@@ -727,14 +722,17 @@ def main():
         torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(False)
+    # the clock stamps sit just outside the timed region (the idle gaps
+    # between them and the steps are a few microseconds of ~55 ms)
+    clock.stamp(0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    clock.stop()
-    clk = clock.window(t0, t1)
+    clock.stamp(1)
+    xcd_mhz = clock.mhz()
     ms_step = (t1 - t0) * 1e3 / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
@@ -746,7 +744,7 @@ def main():
     # algorithmic bytes of the one-launch quantizer pair: bf16 in, codes and
     # scales out, for the activation (1x128 tiles) and the weight (128x128)
     quant_bytes = M * K * 3.03125 + N * K * (3.0 + 4.0 / 16384)
-    clock_mhz = sorted(clk)[len(clk) // 2] if clk else None
+    clock_mhz = sum(xcd_mhz.values()) / len(xcd_mhz) if xcd_mhz else None
 
     line = {
         "metric": METRIC,
@@ -771,11 +769,17 @@ def main():
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic, "kernel": "block_gemm_kernel",
                      "kernel_us": round(g_ms * 1e3, 2)},
-        "clock": {"engine_mhz_timed_median": clock_mhz,
-                  "samples_in_timed_steps": len(clk), "source": clock.source,
+        "clock": {"engine_mhz_timed_mean_over_xcds": round(clock_mhz, 1) if clock_mhz else None,
+                  "engine_mhz_per_xcd": ({str(k): round(v, 1) for k, v in xcd_mhz.items()}
+                                         if xcd_mhz else None),
+                  "source": ("cycle and wall-clock stamps around the timed steps "
+                             "(tests/native/clock_probe.hip)") if xcd_mhz else None,
                   "settle_s": CLOCK_SETTLE_S, "settle_steps": settle_steps,
                   "peak_at_held_clock_TFLOPs": (round(PEAK_FP8_TFLOPS * clock_mhz / 2400.0, 1)
-                                                if clock_mhz else None)},
+                                                if clock_mhz else None),
+                  "frac_of_peak_at_held_clock": (round(gemm_tflops / (PEAK_FP8_TFLOPS * clock_mhz
+                                                                       / 2400.0), 4)
+                                                 if clock_mhz else None)},
         "breakdown_us": {"quant_act_and_weight": round(q_ms * 1e3, 2),
                          "gemm": round(g_ms * 1e3, 2)},
         "quant_in_step": {"GBps": round(quant_bytes / q_ms / 1e6, 1),

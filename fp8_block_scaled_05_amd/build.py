@@ -18,8 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8bs.so")
-# test-only kernels (never part of libfp8bs): tests/native/*.hip, each built
-# into its own library next to its source, with the package's device headers
+# test and measurement helpers (never part of libfp8bs): tests/native/*.hip,
+# each built into its own library next to its source, with the package's
+# device headers (the convert sweep of the GPU tests, bench.py's clock stamps)
 TEST_NATIVE = os.path.join(ROOT, "tests", "native")
 ARCH = "gfx950"
 

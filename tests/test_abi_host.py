@@ -367,3 +367,19 @@ def test_noalloc_gemm_refuses_sizes_beyond_its_buffer(fp8bs):
     assert call(0) == fp8bs.OK
     assert call(64, K=200) == fp8bs.ERR_SHAPE
     assert call(64, out_kind=7) == fp8bs.ERR_DTYPE
+
+
+@pytest.mark.parametrize("name,symbols", [
+    ("convert_sweep", ("fp8bs_test_convert_range",)),
+    ("clock_probe", ("fp8bs_clock_stamp", "fp8bs_wall_clock_khz")),
+])
+def test_helper_libraries_load_and_export(name, symbols):
+    """The test and measurement helpers under tests/native (built by
+    build.py, never part of libfp8bs) load without a GPU and export their
+    entry points."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", f"lib{name}.so")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} is missing: run python -m fp8_block_scaled_05_amd.build")
+    lib = ctypes.CDLL(path)
+    for sym in symbols:
+        assert hasattr(lib, sym), sym
