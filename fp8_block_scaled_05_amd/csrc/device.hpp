@@ -102,11 +102,19 @@ __device__ __forceinline__ float absmax8(const u32x4 v, float m) {
   return m;
 }
 
-// float32 -> bf16 bits, round to nearest even (finite inputs).
+// float32 -> bf16 bits, round to nearest even: gfx950's V_CVT_PK_BF16_F32
+// (one instruction per pair of values), which the compiler selects for a
+// float -> __bf16 conversion on this target.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// (lo, hi) -> one dword: lo in bits 15:0, hi in bits 31:16
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 }  // namespace fp8bs

@@ -392,8 +392,8 @@ __global__ __launch_bounds__(kWaves * 64) void few_rows_kteam_kernel(FewArgs p) 
       if (p.out_bf16) {
         uint16_t* dst = static_cast<uint16_t*>(p.c) + m * p.ldc + n;
         if (vec && nl + 4 <= nrows) {
-          const uint32_t lo = f32_to_bf16_rne(sum[0]) | ((uint32_t)f32_to_bf16_rne(sum[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(sum[2]) | ((uint32_t)f32_to_bf16_rne(sum[3]) << 16);
+          const uint32_t lo = bf16x2_rne(sum[0], sum[1]);
+          const uint32_t hi = bf16x2_rne(sum[2], sum[3]);
           *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
         } else {
           for (int r = 0; r < 4 && nl + r < nrows; ++r) dst[r] = f32_to_bf16_rne(sum[r]);
@@ -592,8 +592,8 @@ __global__ __launch_bounds__(kWaves * 64) void few_rows_shared_kernel(FewArgs p)
       if (p.out_bf16) {
         uint16_t* dst = static_cast<uint16_t*>(p.c) + m * p.ldc + n;
         if (vec && nl + 4 <= nrows) {
-          const uint32_t lo = f32_to_bf16_rne(sum[0]) | ((uint32_t)f32_to_bf16_rne(sum[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(sum[2]) | ((uint32_t)f32_to_bf16_rne(sum[3]) << 16);
+          const uint32_t lo = bf16x2_rne(sum[0], sum[1]);
+          const uint32_t hi = bf16x2_rne(sum[2], sum[3]);
           *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
         } else {
           for (int r = 0; r < 4 && nl + r < nrows; ++r) dst[r] = f32_to_bf16_rne(sum[r]);

@@ -571,27 +571,19 @@ struct Vec {
   typedef T type __attribute__((ext_vector_type(N)));
 };
 
-// fp32 or bf16 output.  Lane (g, l) holds rows 16 i + 4 g + r of the wave's
-// sub-tile and, through the permuted B staging, the FN consecutive columns
-// FN l .. FN l + FN - 1 of the wave's TN columns: one store per row (vector
-// when the row start is aligned for it).
+// The FN values of row r of MFMA row i held by one lane, as the output type:
+// fp32, or bf16 packed two per dword (V_CVT_PK_BF16_F32, nearest even).
 template <class C, int OUT>
-__device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoords& t,
-                                           const v4f (&acc)[C::FM][C::FN], int wm, int wn,
-                                           int lane) {
+struct RowVals {
   using T = typename std::conditional<OUT == kOutBF16, uint16_t, float>::type;
-  const int g4 = lane >> 4, l16 = lane & 15;
-  const int64_t col = t.col0 + wn * C::TN + C::FN * l16;
-  const bool vec = C::FN > 1 && reinterpret_cast<uintptr_t>(t.c) % (C::FN * sizeof(T)) == 0 &&
-                   p.ldc % C::FN == 0;
-  T* const out = reinterpret_cast<T*>(t.c);
+  typename Vec<T, C::FN>::type v;
+  __device__ __forceinline__ RowVals(const v4f (&acc)[C::FM][C::FN], int i, int r) {
+    if constexpr (OUT == kOutBF16 && C::FN % 2 == 0) {
+      typename Vec<uint32_t, C::FN / 2>::type w;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = t.row0 + wm * C::TM + 16 * i + 4 * g4 + r;
-      if (row >= t.row_end) continue;
-      T v[C::FN];
+      for (int q = 0; q < C::FN / 2; ++q) w[q] = bf16x2_rne(acc[i][2 * q][r], acc[i][2 * q + 1][r]);
+      v = __builtin_bit_cast(typename Vec<T, C::FN>::type, w);
+    } else {
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
         if constexpr (OUT == kOutBF16) {
@@ -600,19 +592,60 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoords& 
           v[j] = acc[i][j][r];
         }
       }
+    }
+  }
+};
+
+// fp32 or bf16 output.  Lane (g, l) holds rows 16 i + 4 g + r of the wave's
+// sub-tile and, through the permuted B staging, the FN consecutive columns
+// FN l .. FN l + FN - 1 of the wave's TN columns: one store per row (vector
+// when the row start is aligned for it).  A wave whose whole sub-tile lies
+// inside C (the common case) stores without per-row tests.
+template <class C, int OUT>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoords& t,
+                                           const v4f (&acc)[C::FM][C::FN], int wm, int wn,
+                                           int lane) {
+  using T = typename RowVals<C, OUT>::T;
+  using VT = typename Vec<T, C::FN>::type;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int64_t col = t.col0 + wn * C::TN + C::FN * l16;
+  const bool vec = C::FN > 1 && reinterpret_cast<uintptr_t>(t.c) % (C::FN * sizeof(T)) == 0 &&
+                   p.ldc % C::FN == 0;
+  T* const out = reinterpret_cast<T*>(t.c);
+  const int64_t wrow0 = t.row0 + wm * C::TM;
+  // wave-uniform: every row and column of the wave's sub-tile is inside C
+  const bool inside = vec && wrow0 + C::TM <= t.row_end && t.col0 + (wn + 1) * C::TN <= p.N;
+  if constexpr (C::FN > 1) {
+    if (inside) {
+      T* const base = out + (wrow0 + 4 * g4) * p.ldc + col;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const RowVals<C, OUT> rv(acc, i, r);
+          *reinterpret_cast<VT*>(base + (16 * i + r) * p.ldc) = rv.v;
+        }
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = wrow0 + 16 * i + 4 * g4 + r;
+      if (row >= t.row_end) continue;
+      const RowVals<C, OUT> rv(acc, i, r);
       T* const dst = out + row * p.ldc + col;
       if constexpr (C::FN > 1) {
         if (vec && col + C::FN <= p.N) {
-          typename Vec<T, C::FN>::type w;
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) w[j] = v[j];
-          *reinterpret_cast<typename Vec<T, C::FN>::type*>(dst) = w;
+          *reinterpret_cast<VT*>(dst) = rv.v;
           continue;
         }
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        if (col + j < p.N) dst[j] = v[j];
+        if (col + j < p.N) dst[j] = rv.v[j];
     }
   }
 }
