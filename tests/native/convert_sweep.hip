@@ -1,9 +1,13 @@
-// Test-only kernel (not part of libfp8bs, not declared in fp8bs.h): runs a
-// contiguous range of float32 bit patterns through the library's own device
-// convert (cvt2_e4m3 in device.hpp: clamp to +-448, then the gfx950
-// round-to-nearest-even convert to OCP E4M3) and writes one code per input.
-// The GPU parity test compares the codes of every non-NaN float32 value with
-// the oracle's table-search encoder.
+// Test-only kernels (not part of libfp8bs, not declared in fp8bs.h):
+// - a contiguous range of float32 bit patterns through the library's own
+//   device convert (cvt2_e4m3 in device.hpp: clamp to +-448, then the gfx950
+//   round-to-nearest-even convert to OCP E4M3), one code per input; the GPU
+//   parity test compares the codes of every non-NaN float32 value with the
+//   oracle's table-search encoder;
+// - given float32 bit patterns through the library's bf16 output rounding
+//   (bf16x2_rne and f32_to_bf16_rne in device.hpp: gfx950's
+//   V_CVT_PK_BF16_F32), one bf16 pattern per input, which the test compares
+//   with a CPU round-to-nearest-even conversion.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -47,7 +51,33 @@ __global__ __launch_bounds__(256) void convert_range_kernel(uint32_t first, int6
   }
 }
 
+// out[i] = bf16(in[i]): even i through the paired convert (with in[i + 1]),
+// the last element of an odd count through the single one.
+__global__ __launch_bounds__(256) void bf16_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                   uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+  if (i >= n) return;
+  if (i + 1 < n) {
+    const uint32_t w = fp8bs::bf16x2_rne(__uint_as_float(in[i]), __uint_as_float(in[i + 1]));
+    out[i] = (uint16_t)w;
+    out[i + 1] = (uint16_t)(w >> 16);
+  } else {
+    out[i] = fp8bs::f32_to_bf16_rne(__uint_as_float(in[i]));
+  }
+}
+
 }  // namespace
+
+// Returns 0 on success, 2 for an empty or too large count, or the HIP error
+// of the launch.
+extern "C" int fp8bs_test_bf16_convert(const uint32_t* in, int64_t n, uint16_t* out,
+                                       void* stream) {
+  if (n <= 0 || n > (int64_t(1) << 34)) return 2;
+  const int64_t blocks = (n + 511) / 512;
+  void* args[] = {&in, &n, &out};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(bf16_kernel), dim3((unsigned)blocks),
+                              dim3(256), args, 0, static_cast<hipStream_t>(stream));
+}
 
 // raw != 0: the bare convert (no clamp).  Returns 0 on success, 2 for a
 // range that is empty, wraps past 0xFFFFFFFF or is too large for one launch,

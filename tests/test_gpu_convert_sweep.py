@@ -116,3 +116,45 @@ def test_bare_convert_rounds_448_to_464_down(sign):
     assert np.all(want == ((sign << 7) | 0x7E))
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, f"{bad.size} codes differ, first at {first + bad[0]:#x}: {got[bad[0]]:#x}"
+
+
+def _bf16_patterns():
+    """float32 bit patterns where bf16 rounding has its cases: for every
+    exponent below the NaN/Inf one (subnormals included) and both signs,
+    three settings of the 7 mantissa bits that bf16 keeps (0, 0x40, 0x7F,
+    so that rounding up carries into the exponent and, at the largest
+    exponent, past the largest finite bf16), each with all 2^16 settings of
+    the 16 bits that are rounded away (ties to even included)."""
+    low = np.arange(1 << 16, dtype=np.uint32)
+    out = []
+    for sign in (0, 1):
+        for e in range(255):
+            for mhi in (0x00, 0x40, 0x7F):
+                out.append((sign << 31) | (e << 23) | (mhi << 16) | low)
+    return np.concatenate(out)
+
+
+def test_bf16_output_rounding_matches_cpu_round_to_nearest_even():
+    """The GEMM epilogues write bf16 through gfx950's V_CVT_PK_BF16_F32
+    (device.hpp bf16x2_rne, f32_to_bf16_rne).  Every pattern of
+    _bf16_patterns (100M float32 values, plus an odd tail through the
+    single-value form) must give the bf16 that torch's CPU conversion
+    (round to nearest, ties to even) gives."""
+    lib = _lib()
+    lib.fp8bs_test_bf16_convert.restype = ctypes.c_int
+    lib.fp8bs_test_bf16_convert.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+    pats = np.concatenate([_bf16_patterns(), np.array([0x3F808000, 0x00008000, 0x7F7FFFFF],
+                                                      dtype=np.uint32)])
+    assert pats.size % 2 == 1
+    x = torch.from_numpy(pats.view(np.int32)).to("cuda")
+    out = torch.empty(pats.size, dtype=torch.int16, device="cuda")
+    st = lib.fp8bs_test_bf16_convert(x.data_ptr(), pats.size, out.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
+    assert st == 0, f"launch status {st}"
+    got = out.cpu().numpy().view(np.uint16)
+    want = (torch.from_numpy(pats.view(np.float32)).to(torch.bfloat16)
+            .view(torch.int16).numpy().view(np.uint16))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (f"{bad.size} of {pats.size} differ, first input {pats[bad[0]]:#010x}: "
+                           f"gpu {got[bad[0]]:#06x}, cpu {want[bad[0]]:#06x}")
