@@ -175,6 +175,25 @@ class ClockStamps:
         return {x: sorted(v)[len(v) // 2] for x, v in sorted(per_xcc.items())} or None
 
 
+def _smi_snapshot():
+    """Memory clock (MHz) and socket power (W) from the SMI metrics table, or
+    None.  The table lags the load by about 0.4 s, so a snapshot taken right
+    after the timed steps describes the settle, warm-up and timed steps."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        m = amdsmi.amdsmi_get_gpu_metrics_info(amdsmi.amdsmi_get_processor_handles()[0])
+        out = {}
+        for key, name in (("current_uclk", "mclk_mhz"), ("current_socket_power", "socket_power_w"),
+                          ("average_socket_power", "socket_power_avg_w")):
+            v = m.get(key)
+            if isinstance(v, (int, float)) and 0 < v < 100000:
+                out[name] = v
+        return out or None
+    except Exception:
+        return None
+
+
 def _timeit(torch, fn, iters, warm=5):
     """Median and p10/p90 (ms) of ``iters`` calls of fn(i) after ``warm``."""
     tm = Timer(torch)
@@ -401,7 +420,25 @@ def part_moe(c, iters):
     f2 = 2.0 * Mt * 7168 * 2048
     g1, g2 = tm.med_ms("moe_g1"), tm.med_ms("moe_g2")
     tot = g1 + g2 + tm.med_ms("moe_qa") + tm.med_ms("moe_qw")
+
+    def attainable_ms(N_, K_):
+        """Per-expert roofline: sum over the experts of max(flops / P, bytes / BW),
+        bytes = the expert's weight codes and block scales, its A rows with their
+        scales, and its bf16 output rows (an empty expert reads nothing)."""
+        t = 0.0
+        for g in range(G):
+            m = int(offsets[g + 1] - offsets[g])
+            if m == 0:
+                continue
+            fl = 2.0 * m * N_ * K_
+            by = N_ * K_ + (N_ // 128) * (K_ // 128) * 4 + m * K_ * (1 + 4 / 128) + m * N_ * 2
+            t += max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBPS * 1e9))
+        return t * 1e3
+
+    att = attainable_ms(4096, 7168) + attainable_ms(7168, 2048)
     return {"M_total": Mt, "experts_empty": int((offsets[1:] == offsets[:-1]).sum()),
+            "per_expert_attainable_us": att * 1e3,
+            "gemms_frac_of_per_expert_attainable": att / (g1 + g2),
             "gate_up_us": g1 * 1e3, "gate_up_TFLOPs": f1 / g1 / 1e9,
             "down_us": g2 * 1e3, "down_TFLOPs": f2 / g2 / 1e9,
             "gemms_TFLOPs": (f1 + f2) / (g1 + g2) / 1e9,
@@ -712,6 +749,7 @@ def main():
         run("gemm", lambda: fp8bs.fp8_block_gemm(qa, sa, qw, sw, out=c))
 
     clock = ClockStamps(torch)
+    smi_before = _smi_snapshot()
     # settle the engine clock, then the W warm-up steps
     settle_steps = 0
     t_settle = time.perf_counter()
@@ -733,6 +771,7 @@ def main():
     t1 = time.perf_counter()
     clock.stamp(1)
     xcd_mhz = clock.mhz()
+    smi_after = _smi_snapshot()
     ms_step = (t1 - t0) * 1e3 / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
@@ -779,7 +818,8 @@ def main():
                                                 if clock_mhz else None),
                   "frac_of_peak_at_held_clock": (round(gemm_tflops / (PEAK_FP8_TFLOPS * clock_mhz
                                                                        / 2400.0), 4)
-                                                 if clock_mhz else None)},
+                                                 if clock_mhz else None),
+                  "smi_before_settle": smi_before, "smi_after_timed_steps": smi_after},
         "breakdown_us": {"quant_act_and_weight": round(q_ms * 1e3, 2),
                          "gemm": round(g_ms * 1e3, 2)},
         "quant_in_step": {"GBps": round(quant_bytes / q_ms / 1e6, 1),
