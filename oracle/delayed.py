@@ -18,15 +18,13 @@ Readings taken
   with ``a = max(window maximum, 2^-64)``.
 * Two granularities:
   - ``"tile"``: one history per 1x128 tile position (the online groups, so
-    that only the timeliness of the scale differs).  Ring ``hist[H][KB][M]``;
-    step ``u`` lives in slot ``u % H``; step ``t`` reads all ``H`` slots, then
-    stores its own maxima in slot ``t % H``.
+    that only the timeliness of the scale differs);
   - ``"tensor"``: one history for the whole tensor, the usual practice of
-    earlier FP8 frameworks.  Ring ``hist[H + 2]``; step ``u`` lives in slot
-    ``u % (H + 2)``; step ``t`` reads the ``H`` window slots, raises slot
-    ``t % (H + 2)`` to the current tensor maximum and clears slot
-    ``(t + 1) % (H + 2)`` (the slot the next step raises; it holds step
-    ``t - H - 1``, outside every window still to come).
+    earlier FP8 frameworks.
+  The history is passed in as a plain list, oldest first, of the maxima of
+  the steps in the window.  How a kernel stores it (the device ring and its
+  slot rule) is that kernel's contract, checked by its tests, not part of
+  the method.
 * A group whose window maximum is 0 (no history yet, e.g. the first step of
   a history that starts at zero) is scaled from its own current maximum,
   i.e. online.
@@ -51,40 +49,41 @@ def _tile_max(x):
     return np.max(np.abs(x).reshape(M, KB, TILE), axis=2).T.astype(np.float32)  # [KB][M]
 
 
-def quant_act_1x128_delayed(x_bits, hist, step, mode):
+def quant_act_1x128_delayed(x_bits, window, mode):
     """One step of delayed scaling.
 
-    x_bits: bf16 bits [M][K] (K % 128 == 0); hist: float32 ring (layout per
-    ``mode`` above, not modified); step: t >= 0.
-    Returns ``(q, s, hist_after, stats)``: codes uint8 [M][K]; scales float32
-    [KB][M]; the ring after the step; ``stats`` = (saturated, flushed).
+    x_bits: bf16 bits [M][K] (K % 128 == 0).
+    window: the maxima of the earlier steps in the window, oldest first
+    (possibly empty): float32 arrays [KB][M] for ``"tile"``, floats for
+    ``"tensor"``.
+    Returns ``(q, s, cur, stats)``: codes uint8 [M][K]; scales float32
+    [KB][M]; this step's maxima (float32 [KB][M] per tile, or the tensor
+    maximum as a float32), the entry a caller appends to its history;
+    ``stats`` = (saturated, flushed).
     """
     x = bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16))
     M, K = x.shape
     assert K % TILE == 0
     KB = K // TILE
     cur = _tile_max(x)
-    hist = np.array(hist, dtype=np.float32, copy=True)
     if mode == "tile":
-        H = hist.shape[0]
-        assert hist.shape[1:] == (KB, M)
-        window = np.max(hist, axis=0)
-        hist[step % H] = cur
+        win = np.zeros((KB, M), np.float32)
+        for h in window:
+            h = np.asarray(h, dtype=np.float32)
+            assert h.shape == (KB, M)
+            win = np.maximum(win, h)
+        step_max = cur
     elif mode == "tensor":
-        H = hist.shape[0] - 2
-        assert H >= 1
-        slots = [(step - 1 - d) % (H + 2) for d in range(H)]
-        window = np.full((KB, M), np.max(hist[slots]), dtype=np.float32)
-        w = step % (H + 2)
-        hist[w] = max(hist[w], np.max(cur))
-        hist[(step + 1) % (H + 2)] = 0.0
+        w = np.float32(max([0.0] + [float(h) for h in window]))
+        win = np.full((KB, M), w, dtype=np.float32)
+        step_max = np.float32(np.max(cur))
     else:
         raise ValueError(mode)
-    a = np.where(window > 0, window, cur)
+    a = np.where(win > 0, win, cur)
     s, r = tile_scale(a)
     rr = np.repeat(r.T, TILE, axis=1)  # [M][K]
     y = np.multiply(x, rr, dtype=np.float32)
     q = encode(y)
     saturated = int(np.count_nonzero(np.abs(y) > np.float32(464.0)))
     flushed = int(np.count_nonzero((x != 0) & ((q & 0x7F) == 0)))
-    return q, s, hist, (saturated, flushed)
+    return q, s, step_max, (saturated, flushed)
