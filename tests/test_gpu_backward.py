@@ -57,7 +57,8 @@ def test_token_group_quantizer_strided(fp8bs):
 
 
 @pytest.mark.parametrize("M,N,K,out", [
-    (300, 384, 512, torch.float32),   # 256x256 tiles, ragged M
+    (300, 384, 512, torch.float32),   # 64x128 tiles (too few 256x256 ones), ragged M
+    (1000, 4000, 256, torch.bfloat16),  # 128x256 tiles, ragged M and N
     (257, 200, 256, torch.bfloat16),  # ragged N
     (48, 256, 384, torch.float32),    # few-row tile
     (20, 72, 256, torch.float32),     # 32x32 tile, ragged

@@ -103,7 +103,8 @@ def _closed_form(M, N, K, seed):
 
 @pytest.mark.parametrize("M,N,K", [
     (8, 384, 256),      # few-row tile (64x128)
-    (300, 384, 256),    # 256x256 tiles, ragged M
+    (300, 384, 256),    # 64x128 tiles (too few 256x256 ones), ragged M
+    (1000, 4096, 256),  # 128x256 tiles, ragged M
     (4352, 4096, 128),  # 272 tiles: the last partial round runs as half tiles
 ])
 def test_closed_form_bit_exact(fp8bs, M, N, K):

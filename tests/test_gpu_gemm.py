@@ -183,6 +183,22 @@ def test_few_row_tile_boundaries(fp8bs, M):
     gu.check_gemm(c, C, B)
 
 
+@pytest.mark.parametrize("M,N,K,out", [
+    (300, 700, 384, torch.float32),    # 6 large tiles: 64x128 tiles, one round
+    (1000, 4000, 256, torch.bfloat16),  # 64 large tiles: 128x256 tiles, one round
+    (2100, 7000, 256, torch.bfloat16),  # 252 large tiles: one round of 256x256
+])
+def test_tile_shape_choice(fp8bs, M, N, K, out):
+    """With M > 64 the launch takes 256x256, 128x256 or 64x128 tiles by the
+    rounds of workgroups each would need (the comments give the choice on
+    256 compute units).  Every tile shape sums each output's K groups in the
+    same order; every output is checked against the oracle."""
+    qa, sa, qw, sw = _quantized(M, N, K, case=440 + M)
+    c = _run(fp8bs, qa, sa, qw, sw, out)
+    C, B = oracle.block_gemm(qa, sa, qw, sw)
+    gu.check_gemm(c, C, B)
+
+
 @pytest.mark.parametrize("M,NT", [(200, 257), (100, 257), (512, 129)])
 def test_last_round_split_tiles(fp8bs, M, NT):
     """Rasters of more 256x256 tiles than compute units and not a multiple of
