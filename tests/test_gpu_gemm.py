@@ -199,6 +199,21 @@ def test_tile_shape_choice(fp8bs, M, N, K, out):
     gu.check_gemm(c, C, B)
 
 
+@pytest.mark.parametrize("M,N,split", [
+    (1000, 4000, 500),   # 128x256 tiles whole, 64x128 tiles for the halves
+    (2100, 7000, 1050),  # 256x256 tiles whole, 128x256 tiles for the halves
+])
+def test_tile_shape_does_not_change_results(fp8bs, M, N, split):
+    """The same product computed whole and as two row slices, which the
+    launch runs with different tile shapes: bitwise the same outputs."""
+    K = 384
+    qa, sa, qw, sw = _quantized(M, N, K, case=450 + M)
+    whole = gu.host(_run(fp8bs, qa, sa, qw, sw, torch.float32))
+    top = gu.host(_run(fp8bs, qa[:split], np.ascontiguousarray(sa[:, :split]), qw, sw, torch.float32))
+    bot = gu.host(_run(fp8bs, qa[split:], np.ascontiguousarray(sa[:, split:]), qw, sw, torch.float32))
+    gu.assert_same_bits(whole, np.concatenate([top, bot]), "whole against row slices")
+
+
 @pytest.mark.parametrize("M,NT", [(200, 257), (100, 257), (512, 129)])
 def test_last_round_split_tiles(fp8bs, M, NT):
     """Rasters of more 256x256 tiles than compute units and not a multiple of
