@@ -6,6 +6,7 @@ Importing this module loads ``libfp8bs.so`` from the package directory and
 raises ``ImportError`` if it has not been built (there is no fallback).
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -104,12 +105,28 @@ def _check(status, where):
         raise Fp8bsError(status, where)
 
 
+# The current stream's raw handle; torch's private accessor skips building a
+# Stream object, which costs more than a small kernel's launch.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_NO_SWITCH = contextlib.nullcontext()
+
+
 def _stream(t):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _on(device):
+    """Make ``device`` current for a call (the library's HIP calls act on the
+    current device); no switch when it already is."""
+    if device.index == torch.cuda.current_device():
+        return _NO_SWITCH
+    return torch.cuda.device(device)
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    return t.data_ptr() if t is not None else None
 
 
 def _need_device(*ts):
@@ -191,7 +208,7 @@ def fp8_quant_act_1x128(x, q=None, s=None, lds=None):
         q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty(KB, lds or M, dtype=torch.float32, device=x.device)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         _check(lib.fp8_quant_act_1x128(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), s.stride(0),
                                        _stream(x)), "fp8_quant_act_1x128")
     return q, s
@@ -232,7 +249,7 @@ def fp8_quant_act_1x128_delayed(x, hist, step, mode="tile", q=None, s=None, stat
         q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty(KB, M, dtype=torch.float32, device=x.device)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         _check(lib.fp8_quant_act_1x128_delayed(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s),
                                                s.stride(0), m, _ptr(hist), ldh, H, step,
                                                _ptr(stats), _stream(x)),
@@ -253,7 +270,7 @@ def fp8_quant_w_128x128(w, q=None, s=None):
         q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
     if s is None:
         s = torch.empty((N + 127) // 128, KB, dtype=torch.float32, device=w.device)
-    with torch.cuda.device(w.device):
+    with _on(w.device):
         _check(lib.fp8_quant_w_128x128(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _stream(w)),
                "fp8_quant_w_128x128")
     return q, s
@@ -284,7 +301,7 @@ def fp8_quant_linear(x, w, q=None, s=None, qw=None, sw=None):
         qw = torch.empty(N, K, dtype=torch.uint8, device=w.device)
     if sw is None:
         sw = torch.empty((N + 127) // 128, KB, dtype=torch.float32, device=w.device)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         _check(lib.fp8_quant_linear(_ptr(x), M, K, ldx, _ptr(q), _ld(q), _ptr(s), s.stride(0),
                                     _ptr(w), N, ldw, _ptr(qw), _ld(qw), _ptr(sw), _stream(x)),
                "fp8_quant_linear")
@@ -312,7 +329,7 @@ def fp8_quant_w_128x128_t(w, q=None, s=None, qt=None, st=None):
     s = torch.empty(NB, KB, dtype=torch.float32, device=dev) if s is None else s
     qt = torch.empty(K, N, dtype=torch.uint8, device=dev) if qt is None else qt
     st = torch.empty(KB, NB, dtype=torch.float32, device=dev) if st is None else st
-    with torch.cuda.device(w.device):
+    with _on(w.device):
         _check(lib.fp8_quant_w_128x128_t(_ptr(w), N, K, ldw, _ptr(q), _ld(q), _ptr(s), _ptr(qt),
                                          _ld(qt), _ptr(st), _stream(w)), "fp8_quant_w_128x128_t")
     return q, s, qt, st
@@ -334,7 +351,7 @@ def fp8_quant_act_128x1_t(x, qt=None, st=None):
         qt = torch.empty(N, M, dtype=torch.uint8, device=x.device)
     if st is None:
         st = torch.empty(M // 128, N, dtype=torch.float32, device=x.device)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         _check(lib.fp8_quant_act_128x1_t(_ptr(x), M, N, ldx, _ptr(qt), _ld(qt), _ptr(st),
                                          st.stride(0), _stream(x)), "fp8_quant_act_128x1_t")
     return qt, st
@@ -356,7 +373,7 @@ def fp8_block_gemm_rowscaled(a, sa, b, sb, out=None, out_dtype=torch.float32):
     _need_device(a, sa, b, sb, out)
     if out is None:
         out = torch.empty(M, N, dtype=out_dtype, device=a.device)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         _check(lib.fp8_block_gemm_rowscaled(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
                                             _ld(b), _ptr(sb), sb.stride(0), _ptr(out), _ld(out),
                                             _out_kind(out.dtype), M, N, K, _stream(a)),
@@ -388,7 +405,7 @@ def fp8_block_kgrouped_gemm_rowscaled(a, sa, b, sb, group_offsets, out=None,
     _need_device(a, sa, b, sb, group_offsets, out)
     if out is None:
         out = torch.empty(G, M, N, dtype=out_dtype, device=a.device)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         _check(lib.fp8_block_kgrouped_gemm_rowscaled(
             _ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b), _ld(b), _ptr(sb), sb.stride(0),
             _ptr(out), out.stride(1), out.stride(0), _out_kind(out.dtype), _ptr(group_offsets),
@@ -450,7 +467,7 @@ def fp8_block_gemm(a, sa, b, sb, out=None, out_dtype=torch.bfloat16, workspace=N
         out = torch.empty(M, N, dtype=out_dtype, device=a.device)
     workspace, ws_bytes = _workspace(a_kind, M, N, K, workspace, a.device)
     ldsa = sa.stride(0) if sa is not None else 0
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         _check(lib.fp8_block_gemm(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
                                   _ptr(sb), _ptr(out), _ld(out), _out_kind(out.dtype), M, N, K,
                                   _ptr(workspace), ws_bytes, _stream(a)), "fp8_block_gemm")
@@ -471,7 +488,7 @@ def fp8_block_gemm_bf16_noalloc(a, sa, b, sb, out):
     _mat(out, "out", M, N, out.dtype)
     _need_device(a, sa, b, sb, out)
     ldsa = sa.stride(0) if sa is not None else 0
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         _check(lib.fp8_block_gemm_bf16_noalloc(_ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b), _ld(b),
                                                _ptr(sb), _ptr(out), _ld(out),
                                                _out_kind(out.dtype), M, N, K, _stream(a)),
@@ -509,7 +526,7 @@ def fp8_block_grouped_gemm(a, sa, b, sb, group_offsets, out=None, out_dtype=torc
     _need_device(a, sa, b, sb, group_offsets, out)
     if out is None:
         out = torch.empty(M_total, N, dtype=out_dtype, device=a.device)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         _check(lib.fp8_block_grouped_gemm(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
                                           b.stride(1), b.stride(0), _ptr(sb), _ptr(out), _ld(out),
                                           _out_kind(out.dtype), _ptr(group_offsets), G, M_total, N,
@@ -545,7 +562,7 @@ def fp8_block_gemm_e4m3_out(a, sa, b, sb, qc=None, sc=None, workspace=None):
     qc, sc = _e4m3_outputs(M, N, qc, sc, a.device)
     workspace, ws_bytes = _workspace(a_kind, M, N, K, workspace, a.device)
     ldsa = sa.stride(0) if sa is not None else 0
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         _check(lib.fp8_block_gemm_e4m3_out(a_kind, _ptr(a), _ld(a), _ptr(sa), ldsa, _ptr(b),
                                            _ld(b), _ptr(sb), _ptr(qc), _ld(qc), _ptr(sc),
                                            sc.stride(0), M, N, K, _ptr(workspace), ws_bytes,
@@ -564,7 +581,7 @@ def fp8_block_grouped_gemm_e4m3_out(a, sa, b, sb, group_offsets, qc=None, sc=Non
     _e4m3_check(M_total, N, qc, sc)
     _need_device(a, sa, b, sb, group_offsets, qc, sc)
     qc, sc = _e4m3_outputs(M_total, N, qc, sc, a.device)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         _check(lib.fp8_block_grouped_gemm_e4m3_out(_ptr(a), _ld(a), _ptr(sa), sa.stride(0), _ptr(b),
                                                    b.stride(1), b.stride(0), _ptr(sb), _ptr(qc),
                                                    _ld(qc), _ptr(sc), sc.stride(0),
