@@ -206,6 +206,28 @@ def _timeit(torch, fn, iters, warm=5):
     return ts[len(ts) // 2], ts[len(ts) // 10], ts[(len(ts) * 9) // 10]
 
 
+def _streamed(torch, fn, iters, warm=5):
+    """Milliseconds per call of ``iters`` back-to-back calls of fn(i) between
+    one pair of events on the stream (the per-call events of _timeit add
+    their own packets between the kernels)."""
+    for i in range(warm):
+        fn(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def _streamed_rate(torch, fn, iters, byt):
+    ms = _streamed(torch, fn, iters)
+    return {"streamed_us": ms * 1e3, "streamed_GBps": byt / ms / 1e6,
+            "streamed_frac_hbm": byt / ms / 1e6 / PEAK_HBM_GBPS}
+
+
 def _rate(byt, ms):
     gbps = byt / ms / 1e6
     return {"GBps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS}
@@ -228,11 +250,11 @@ def part_act_quant(c, iters):
     xs = [synth.act(Mq, Kq, case=synth.QUANT.case_id, tensor=i, device="cuda") for i in range(4)]
     qs = [torch.empty(Mq, Kq, dtype=torch.uint8, device="cuda") for _ in range(4)]
     ss = [torch.empty(Kq // 128, Mq, dtype=torch.float32, device="cuda") for _ in range(4)]
-    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_quant_act_1x128(xs[i % 4], qs[i % 4],
-                                                                        ss[i % 4]), iters)
+    call = lambda i: fp8bs.fp8_quant_act_1x128(xs[i % 4], qs[i % 4], ss[i % 4])
+    med, p10, p90 = _timeit(torch, call, iters)
     byt = Mq * Kq * 3.03125
     return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(byt, med),
-            "bytes": byt}
+            "bytes": byt, **_streamed_rate(torch, call, iters, byt)}
 
 
 def part_hbm_copy(c, iters):
@@ -244,9 +266,10 @@ def part_hbm_copy(c, iters):
     n = int(n) // 16 * 16
     src = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i) for i in range(4)]
     dst = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(4)]
-    med, p10, p90 = _timeit(torch, lambda i: dst[i % 4].copy_(src[i % 4]), iters)
+    call = lambda i: dst[i % 4].copy_(src[i % 4])
+    med, p10, p90 = _timeit(torch, call, iters)
     return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(2 * n, med),
-            "bytes": 2 * n}
+            "bytes": 2 * n, **_streamed_rate(torch, call, iters, 2 * n)}
 
 
 def part_weight_quant(c, iters):
@@ -256,11 +279,11 @@ def part_weight_quant(c, iters):
           for i in range(2)]
     qws = [torch.empty(N, K, dtype=torch.uint8, device="cuda") for _ in range(2)]
     sws = [torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda") for _ in range(2)]
-    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_quant_w_128x128(ws[i % 2], qws[i % 2],
-                                                                        sws[i % 2]), iters)
+    call = lambda i: fp8bs.fp8_quant_w_128x128(ws[i % 2], qws[i % 2], sws[i % 2])
+    med, p10, p90 = _timeit(torch, call, iters)
     byt = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
     return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(byt, med),
-            "bytes": byt}
+            "bytes": byt, **_streamed_rate(torch, call, iters, byt)}
 
 
 def part_quant_pair(c, iters):
@@ -275,11 +298,11 @@ def part_quant_pair(c, iters):
             torch.empty(K // 128, Mq, dtype=torch.float32, device="cuda"),
             torch.empty(N, K, dtype=torch.uint8, device="cuda"),
             torch.empty(N // 128, K // 128, dtype=torch.float32, device="cuda")) for _ in range(2)]
-    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_quant_linear(xs[i % 2], ws[i % 2],
-                                                                     *out[i % 2]), iters)
+    call = lambda i: fp8bs.fp8_quant_linear(xs[i % 2], ws[i % 2], *out[i % 2])
+    med, p10, p90 = _timeit(torch, call, iters)
     byt = Mq * K * 3.03125 + N * K * 2 + N * K + (N // 128) * (K // 128) * 4
     return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(byt, med),
-            "bytes": byt}
+            "bytes": byt, **_streamed_rate(torch, call, iters, byt)}
 
 
 def _skinny(c, iters, Ms):
@@ -293,11 +316,13 @@ def _skinny(c, iters, Ms):
     sa_o = torch.empty(K // 128, Ms, dtype=torch.float32, device="cuda")
     wsp = torch.empty(fp8bs.workspace_bytes(fp8bs.OP_GEMM_BF16, Ms, N, K), dtype=torch.uint8,
                       device="cuda")
-    med, p10, p90 = _timeit(torch, lambda i: fp8bs.fp8_block_gemm(
-        x, sa_o, wq[i % 4][0], wq[i % 4][1], out=cs, workspace=wsp), iters)
+    call = lambda i: fp8bs.fp8_block_gemm(x, sa_o, wq[i % 4][0], wq[i % 4][1], out=cs,
+                                          workspace=wsp)
+    med, p10, p90 = _timeit(torch, call, iters)
     byt = N * K + (N // 128) * (K // 128) * 4 + Ms * K * 2 + Ms * N * 2
     return {"us": med * 1e3, "p10_us": p10 * 1e3, "p90_us": p90 * 1e3, **_rate(byt, med),
             "TFLOPs": 2 * Ms * N * K / med / 1e9, "bytes": byt,
+            **_streamed_rate(torch, call, iters, byt),
             "activation_quantized": "inside the GEMM kernel" if Ms <= 16 else
             "by a separate launch before the GEMM"}
 
