@@ -33,11 +33,12 @@ using LargeTail = gemm::Cfg<128, 256, 2, 4, 2, 4>;
 using Rows32Cfg = gemm::Cfg<32, 32, 1, 2, 4, 1>;
 using Rows64Cfg = gemm::Cfg<64, 128, 1, 4, 4, 1>;
 
-// Tile shape for M > 64: the fewest estimated rounds of workgroups, a round
-// of 256x256, 128x256 and 64x128 (four-stage) tiles weighing 100, 77 and 40
-// (measured per tile and K group on MI355X with one round or two); the
-// 256x256 launch runs a last partial round of at most half the compute
-// units as 128x256 tiles, half a round.
+// Tile shape for M > 64: the least estimated time, counted in rounds of
+// workgroups (one workgroup per compute unit), a round of 256x256, 128x256
+// and 64x128 (four-stage) tiles taking 100, 77 and 40 (relative times per
+// round at equal K, measured on MI355X with one or two rounds); the 256x256
+// launch runs a last partial round of at most half the compute units as
+// 128x256 tiles, half a round.
 enum class Tiles { kLarge, kHalf, kSmall };
 Tiles pick_tiles(const GemmArgs& a) {
   const int64_t cus = gemm::device_cus();
