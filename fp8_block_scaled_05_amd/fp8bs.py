@@ -134,9 +134,10 @@ def _need_device(*ts):
     for t in ts:
         if t is None:
             continue
-        if not t.is_cuda:
+        d = t.device
+        if d.type != "cuda":
             raise ValueError("libfp8bs works on GPU tensors only")
-        devices.add(t.device)
+        devices.add(d)
     if len(devices) > 1:
         raise ValueError("all tensors of a call must be on one GPU, got "
                          f"{sorted(map(str, devices))}")
@@ -151,17 +152,19 @@ def _mat(t, name, rows, cols, dtype, ld=None):
         return
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols:
+    shape = t.shape
+    if len(shape) != 2 or shape[0] < rows or shape[1] < cols:
         raise ValueError(f"{name} must be a 2-D tensor of at least [{rows}][{cols}], "
-                         f"got {list(t.shape)}")
-    if t.numel() == 0:
+                         f"got {list(shape)}")
+    if shape[0] == 0 or shape[1] == 0:
         return  # nothing is read or written; an empty tensor's strides are arbitrary
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    row, col = t.stride()
+    if shape[1] > 1 and col != 1:
         raise ValueError(f"{name} must have unit column stride")
-    if rows > 1 and t.stride(0) < cols:
-        raise ValueError(f"{name} rows overlap (row stride {t.stride(0)} < {cols})")
-    if ld is not None and rows > 1 and t.stride(0) != ld:
-        raise ValueError(f"{name} must have row stride {ld}, got {t.stride(0)}")
+    if rows > 1 and row < cols:
+        raise ValueError(f"{name} rows overlap (row stride {row} < {cols})")
+    if ld is not None and rows > 1 and row != ld:
+        raise ValueError(f"{name} must have row stride {ld}, got {row}")
 
 
 def _rowmajor(t, name):
